@@ -1,0 +1,203 @@
+"""CPU oracle of the PIVOT query-group indexer (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's CPU-baseline leg; never by the product package.  The arithmetic
+lives in pivot_oracle.c (plain single-threaded C, double accumulation); this
+file only marshals numpy arrays.
+
+Pinned functions (see tests/test_oracle_*.py): codecs, score, top-m, dense,
+proxy, Reuse, Refine, decode grouping.  Parity on realistic float inputs is
+pinned only through invariants and the closed-form/worked examples.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SRC = os.path.join(_HERE, "pivot_oracle.c")
+
+BF16, FP8 = 0, 1
+DENSE, REUSE, REFINE = 0, 1, 2
+MODES = {"dense": DENSE, "reuse": REUSE, "refine": REFINE}
+
+
+def build(force: bool = False) -> str:
+    """Compile pivot_oracle.c with gcc (plain -O2, IEEE binary32/binary64, no
+    contraction of multiply-adds, single-threaded)."""
+    if force or not os.path.exists(_LIB_PATH):
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-o", _LIB_PATH, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+    return _LIB_PATH
+
+
+class _View(C.Structure):
+    _fields_ = [("H", C.c_int), ("D", C.c_int), ("dtype", C.c_int),
+                ("q", C.c_void_p), ("q_scale", C.c_void_p), ("w", C.c_void_p),
+                ("k", C.c_void_p), ("k_scale", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = C.CDLL(_LIB_PATH)
+        i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+        f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+        L.orc_bf16_value.restype = C.c_double
+        L.orc_bf16_value.argtypes = [C.c_uint16]
+        L.orc_e4m3_value.restype = C.c_double
+        L.orc_e4m3_value.argtypes = [C.c_uint8]
+        L.orc_bf16_from_f32.restype = C.c_uint16
+        L.orc_bf16_from_f32.argtypes = [C.c_float]
+        L.orc_e4m3_from_f32.restype = C.c_uint8
+        L.orc_e4m3_from_f32.argtypes = [C.c_float]
+        L.orc_topk.argtypes = [C.c_int, i32p, f64p, C.c_int, i32p]
+        L.orc_proxy.argtypes = [C.POINTER(_View), C.c_int, C.c_int, C.c_void_p,
+                                C.POINTER(C.c_float), C.c_void_p]
+        L.orc_dense_rows.argtypes = [C.POINTER(_View), i32p, C.c_int, C.c_int, i32p]
+        L.orc_group.argtypes = [C.POINTER(_View), C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                C.c_int, i32p, C.c_void_p, C.c_void_p]
+        L.orc_prefill_groups.argtypes = [C.POINTER(_View), C.c_int, C.c_int, C.c_int, C.c_int,
+                                         C.c_int, i32p, C.c_int, i32p, C.c_void_p]
+        L.orc_score_row.argtypes = [C.POINTER(_View), C.c_int, C.c_int, f64p]
+        L.orc_score_pairs.argtypes = [C.POINTER(_View), i32p, i32p, C.c_int, f64p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class View:
+    """Keeps the numpy arrays alive and exposes them as an orc_view.
+
+    q [R,H,D] codes, q_scale [R] or None, w [R,H], k [N,D] codes, k_scale [N] or None."""
+
+    def __init__(self, dtype, q, q_scale, w, k, k_scale):
+        self.dtype = BF16 if dtype in ("bf16", BF16) else FP8
+        code_t = np.uint16 if self.dtype == BF16 else np.uint8
+        self.q = np.ascontiguousarray(q, dtype=code_t)
+        self.k = np.ascontiguousarray(k, dtype=code_t)
+        self.w = np.ascontiguousarray(w, dtype=np.float32)
+        self.q_scale = None if q_scale is None else np.ascontiguousarray(q_scale, np.float32)
+        self.k_scale = None if k_scale is None else np.ascontiguousarray(k_scale, np.float32)
+        if self.dtype == FP8 and (self.q_scale is None or self.k_scale is None):
+            raise ValueError("fp8 views need q_scale and k_scale")
+        self.H, self.D = int(self.q.shape[-2]), int(self.q.shape[-1])
+        self.c = _View(self.H, self.D, self.dtype, _ptr(self.q), _ptr(self.q_scale),
+                       _ptr(self.w), _ptr(self.k), _ptr(self.k_scale))
+
+    @classmethod
+    def of(cls, inp):
+        return cls(inp.dtype, inp.q, inp.q_scale, inp.w, inp.k, inp.k_scale)
+
+
+def bf16_value(code):
+    return lib().orc_bf16_value(int(code))
+
+
+def e4m3_value(code):
+    return lib().orc_e4m3_value(int(code))
+
+
+def bf16_from_f32(x):
+    return lib().orc_bf16_from_f32(float(x))
+
+
+def e4m3_from_f32(x):
+    return lib().orc_e4m3_from_f32(float(x))
+
+
+def topk(scores, m, pos=None):
+    scores = np.ascontiguousarray(scores, np.float64)
+    n = scores.shape[0]
+    pos = np.arange(n, dtype=np.int32) if pos is None else np.ascontiguousarray(pos, np.int32)
+    out = np.empty(m, np.int32)
+    lib().orc_topk(n, pos, scores, m, out)
+    return out
+
+
+def proxy(view: View, row0: int, n: int):
+    code_t = np.uint16 if view.dtype == BF16 else np.uint8
+    codes = np.empty((view.H, view.D), code_t)
+    wbar = np.empty(view.H, np.float32)
+    s = C.c_float(0.0)
+    lib().orc_proxy(C.byref(view.c), row0, n, codes.ctypes.data, C.byref(s), wbar.ctypes.data)
+    return codes, np.float32(s.value), wbar
+
+
+def dense_rows(view: View, rows, topk_: int):
+    rows = np.ascontiguousarray(rows, np.int32)
+    out = np.empty((rows.shape[0], topk_), np.int32)
+    lib().orc_dense_rows(C.byref(view.c), rows, rows.shape[0], topk_, out)
+    return out
+
+
+def group(view: View, row0: int, pos0: int, n: int, topk_: int, C_: int, mode):
+    """One group; returns (out [n,topk], cand [m] or None, proxy scores [pos0+n])."""
+    mode = MODES.get(mode, mode)
+    out = np.empty((n, topk_), np.int32)
+    m = C_ if mode == REFINE else topk_
+    cand = np.empty(m, np.int32) if mode != DENSE else None
+    psc = np.empty(pos0 + n, np.float64) if mode != DENSE else None
+    lib().orc_group(C.byref(view.c), row0, pos0, n, topk_, C_, mode, out,
+                    _ptr(cand), _ptr(psc))
+    return out, cand, psc
+
+
+def prefill_groups(view: View, L: int, g: int, topk_: int, C_: int, mode, groups):
+    """Rows of the listed prefill groups (packed) and their candidate lists."""
+    mode = MODES.get(mode, mode)
+    groups = np.ascontiguousarray(groups, np.int32)
+    nrows = int(sum(min(g, L - int(j) * g) for j in groups))
+    out = np.empty((nrows, topk_), np.int32)
+    m = C_ if mode == REFINE else topk_
+    cand = np.empty((groups.shape[0], m), np.int32) if mode != DENSE else None
+    lib().orc_prefill_groups(C.byref(view.c), L, g, topk_, C_, mode, groups, groups.shape[0],
+                             out, _ptr(cand))
+    return out, cand
+
+
+def group_rows(L: int, g: int, groups):
+    """Query positions covered by the listed groups, in the packed order."""
+    return np.concatenate([np.arange(int(j) * g, min(L, int(j) * g + g)) for j in groups]
+                          ).astype(np.int32)
+
+
+def score_row(view: View, row: int, n: int):
+    out = np.empty(n, np.float64)
+    lib().orc_score_row(C.byref(view.c), row, n, out)
+    return out
+
+
+def score_pairs(view: View, rows, keys):
+    rows = np.ascontiguousarray(rows, np.int32)
+    keys = np.ascontiguousarray(keys, np.int32)
+    out = np.empty(rows.shape[0], np.float64)
+    lib().orc_score_pairs(C.byref(view.c), rows, keys, rows.shape[0], out)
+    return out
+
+
+def decode_view(dec, b: int) -> View:
+    """View of sequence b of a decode step: its g query rows and its key cache."""
+    qs = None if dec.q_scale is None else dec.q_scale[b]
+    ks = None if dec.k_scale is None else dec.k_scale[b]
+    return View(dec.dtype, dec.q[b], qs, dec.w[b], dec.k[b], ks)
+
+
+def decode_seq(dec, b: int, topk_: int, C_: int, mode):
+    """Decode grouping (arXiv:2607.24593 abstract: the queries decoded together
+    in one MTP step form the group): members at positions n_b-g..n_b-1, the
+    shared scan covers the whole cache [0, n_b)."""
+    n = int(dec.cache_len[b])
+    return group(decode_view(dec, b), 0, n - dec.g, dec.g, topk_, C_, mode)
