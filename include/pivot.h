@@ -1,0 +1,185 @@
+/*
+ * pivot.h -- C ABI of the PIVOT query-group indexer for MI355X (gfx950).
+ *
+ * The indexer of token-level sparse attention picks, for each query, the
+ * positions of the top-k earlier tokens under an indexer score; the
+ * tutorial "Sparse Attention의 Indexer" (ai-systems-engineering.com, Figure 1
+ * and the section on how the selection changes during generation) shows the
+ * plain version: score every key up to and including the query's own
+ * position, keep the k best positions.  PIVOT ("PIVOT: Efficient Query-Group
+ * Indexing for Token-Level Sparse Attention", arXiv:2607.24593, English
+ * abstract on the arxivdaily page) replaces the per-query scan: a group of
+ * nearby queries is averaged into one proxy query, the proxy scans the full
+ * causal prefix once and keeps a candidate set, and then either every member
+ * receives the proxy's top-k (PIVOT-Reuse) or every member re-scores the
+ * candidates with its own query and keeps its own top-k (PIVOT-Refine).
+ * Prefill groups are fixed-size runs of consecutive queries; in decode the
+ * group is the set of queries one multi-token-prediction step produces.
+ *
+ * Score of query q (H heads of dimension D, head weights w) against key k_s
+ * (one key per token, shared by all heads):
+ *     S(q, s) = sum_h w[h] * max(0, q[h] . k_s)
+ * with, for fp8, the positive per-token scales applied as s_q * s_k * S(codes).
+ *
+ * Conventions for every entry point below:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates or frees device memory.  Scratch memory comes from the
+ *    caller's `workspace` (256-byte aligned), sized by the *_workspace_size
+ *    functions; a larger workspace lets the library process more score rows
+ *    per pass, a smaller one (down to the size for one row block) is accepted.
+ *  - Inputs are read-only; `out` and `workspace` must not alias any input.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronising.  Calls sharing a workspace
+ *    must be ordered on one stream.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    non-zero status nothing was launched and `out` is untouched.  A failed
+ *    launch returns PIVOT_ERR_HIP.  pivot_last_error() gives a message for the
+ *    last failure on the calling thread.
+ *  - Codes: bf16 (uint16 storage) or OCP FP8 E4M3FN (uint8 storage, finite
+ *    max 448) with one float32 scale per token, which must be > 0.  NaN or Inf
+ *    inputs are outside the contract.
+ *  - Supported shapes: 1 <= H <= 64; D in {32, 64, 128, 256} for bf16 and
+ *    {64, 128, 256} for fp8.  q and k 16-byte aligned, w / scales / out
+ *    4-byte aligned.
+ *  - Output rows list positions in ascending order; a row holding fewer than
+ *    topk positions is padded with -1 at its tail.  Among equal scores the
+ *    lower position is preferred, so every output is unique.
+ */
+#ifndef PIVOT_H
+#define PIVOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PIVOT_OK = 0,
+  PIVOT_ERR_NULL = 1,        /* a required pointer is NULL */
+  PIVOT_ERR_SHAPE = 2,       /* L, B, H, D, Lmax out of range or unsupported */
+  PIVOT_ERR_PARAM = 3,       /* g, topk, C, mode or dtype invalid (e.g. C < topk for Refine) */
+  PIVOT_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+  PIVOT_ERR_WORKSPACE = 5,   /* workspace smaller than the minimum */
+  PIVOT_ERR_HIP = 6          /* a kernel launch failed */
+} pivot_status_t;
+
+typedef enum {
+  PIVOT_MODE_DENSE = 0,  /* every query scans its own prefix (g is ignored) */
+  PIVOT_MODE_REUSE = 1,  /* PIVOT-Reuse: members share the proxy top-k */
+  PIVOT_MODE_REFINE = 2  /* PIVOT-Refine: members re-score the proxy top-C */
+} pivot_mode_t;
+
+typedef enum { PIVOT_BF16 = 0, PIVOT_FP8_E4M3 = 1 } pivot_dtype_t;
+
+int pivot_version(void);
+const char* pivot_status_string(int status);
+const char* pivot_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Prefill: one sequence of L queries over its own L keys (query t sits at
+ * position t and sees keys 0..t).  Groups of g consecutive queries start at
+ * position 0; the last group holds the remaining L mod g queries when g does
+ * not divide L.  The proxy of group j (members j*g..e_j) scans keys 0..e_j.
+ *
+ *   q       [L][H][D] codes           q_scale [L] float (fp8 only, else NULL)
+ *   w       [L][H] float head weights
+ *   k       [L][D] codes              k_scale [L] float (fp8 only, else NULL)
+ *   out     [L][topk] int32 positions
+ *   C       candidate-set size for Refine (C >= topk); ignored otherwise
+ * Returns a pivot_status_t.
+ * ------------------------------------------------------------------------- */
+size_t pivot_workspace_size(int L, int H, int D, int g, int topk, int C, int mode, int dtype);
+size_t pivot_workspace_min_size(int L, int H, int D, int g, int topk, int C, int mode, int dtype);
+int pivot_indexer(const void* q, const float* q_scale, const float* w, const void* k,
+                  const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
+                  int dtype, int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode: one multi-token-prediction step for B sequences.  Sequence b holds
+ * cache_len[b] keys (the g new ones included) and decodes g queries at
+ * positions cache_len[b]-g .. cache_len[b]-1; they form one group whose proxy
+ * scans the whole cache 0..cache_len[b]-1.
+ *
+ *   q         [B][g][H][D] codes      q_scale [B][g] float (fp8 only)
+ *   w         [B][g][H] float
+ *   k_cache   [B][Lmax][D] codes      k_scale [B][Lmax] float (fp8 only)
+ *   cache_len [B] int32, DEVICE memory; precondition g <= cache_len[b] <= Lmax
+ *             (a sequence breaking it receives rows of -1)
+ *   out       [B][g][topk] int32 positions
+ * ------------------------------------------------------------------------- */
+size_t pivot_decode_workspace_size(int B, int Lmax, int H, int D, int g, int topk, int C,
+                                   int mode, int dtype);
+int pivot_indexer_decode(const void* q, const float* q_scale, const float* w,
+                         const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                         int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                         int dtype, int32_t* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Single steps of the prefill path, for step-level checks.
+ *
+ * pivot_proxy_mean: the proxy of every group (arXiv:2607.24593 abstract: one
+ * proxy query stands for the whole group; molayo1419.me "PIVOT explained",
+ * section How It Works: the proxy is the mean of the group).  Members are added
+ * in ascending position in binary32 and divided by the member count; w is
+ * averaged the same way.  bf16: the mean is rounded to nearest even.  fp8: a
+ * fresh scale s = amax/448 (1 if all zero) and codes rounded to nearest even,
+ * saturating at +-448.  A one-member group is copied unchanged.  Also serves
+ * decode rows laid out [B][g][...] by passing L = B*g.
+ *   qbar [G][H][D] codes, qbar_scale [G] float (written for both dtypes,
+ *   1 for bf16), wbar [G][H] float, G = ceil(L/g).
+ *
+ * pivot_candidates: proxy mean, the proxy's full-prefix scan and its top-m
+ * (m = C for REFINE, topk for REUSE): cand [G][m] ascending, -1 padded.
+ *
+ * pivot_decode_candidates: the same three steps for a decode step (one group
+ * per sequence, the scan covering its whole cache): cand [B][m].
+ * ------------------------------------------------------------------------- */
+int pivot_proxy_mean(const void* q, const float* q_scale, const float* w, int L, int H, int D,
+                     int g, int dtype, void* qbar, float* qbar_scale, float* wbar, void* stream);
+int pivot_candidates(const void* q, const float* q_scale, const float* w, const void* k,
+                     const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
+                     int dtype, int32_t* cand, void* workspace, size_t workspace_bytes,
+                     void* stream);
+int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,
+                            const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                            int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                            int dtype, int32_t* cand, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-kernel timing for measurement tools.  While enabled (process-wide),
+ * every kernel the library launches is bracketed by two HIP events recorded on
+ * its launch stream.  pivot_profile_read waits for the recorded events, writes
+ * the summed milliseconds and the launch count of each kernel class
+ * (PIVOT_K_* order; arrays of n entries) and clears the record.  Disabled by
+ * default.  Returns a pivot_status_t.
+ * ------------------------------------------------------------------------- */
+enum {
+  PIVOT_K_PROXY = 0,        /* proxy mean */
+  PIVOT_K_SCAN = 1,         /* prefill full-prefix scan (proxies or dense queries) */
+  PIVOT_K_SELECT = 2,       /* proxy top-m / dense top-k */
+  PIVOT_K_REFINE = 3,       /* Refine gather-score */
+  PIVOT_K_MEMBER_SELECT = 4,/* Refine member top-k */
+  PIVOT_K_BROADCAST = 5,    /* Reuse broadcast */
+  PIVOT_K_DECODE_SCAN = 6,  /* decode key-cache scan */
+  PIVOT_K_COUNT = 7
+};
+int pivot_profile_enable(int on);
+int pivot_profile_read(double* ms, long long* launches, int n);
+
+/* ---------------------------------------------------------------------------
+ * Layout self-test of the matrix-core instructions the scoring kernels use
+ * (32x32 bf16 and fp8 tiles): writes, for each lane l and accumulator i,
+ * the row, the column and a k-pairing probe into out[3][2][64][16] (device,
+ * int32): [0] rows, [1] columns, [2] pairing (1 where the lane halves' k
+ * slices pair up as the kernels assume), for bf16 then fp8.
+ * ------------------------------------------------------------------------- */
+int pivot_selftest_mfma_layout(int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PIVOT_H */

@@ -196,8 +196,8 @@ def decode_view(dec, b: int) -> View:
 
 
 def decode_seq(dec, b: int, topk_: int, C_: int, mode):
-    """Decode grouping (arXiv:2607.24593 abstract: the queries decoded together
-    in one MTP step form the group): members at positions n_b-g..n_b-1, the
+    """Decode grouping (arXiv:2607.24593 abstract: in decode a group is the set
+    of queries one MTP step produces): members at positions n_b-g..n_b-1, the
     shared scan covers the whole cache [0, n_b)."""
     n = int(dec.cache_len[b])
     return group(decode_view(dec, b), 0, n - dec.g, dec.g, topk_, C_, mode)

@@ -8,7 +8,7 @@
  *   [ABS]  arxivdaily page for arXiv:2607.24593, "PIVOT: Efficient Query-Group
  *          Indexing for Token-Level Sparse Attention", English abstract.
  *   [BLOG] molayo1419.me, "PIVOT explained: from paper to working code",
- *          section "How It Works" (group / proxy_q = mean(group) pseudocode).
+ *          section "How It Works" (pseudocode: the proxy is the group mean).
  *   [TUT]  ai-systems-engineering.com, "Sparse Attention의 Indexer", Figure 1
  *          (score by dot product, top-3 of positions) and the section on how
  *          the selection changes during generation (causal prefix, self
@@ -101,9 +101,16 @@ uint8_t orc_e4m3_from_f32(float x) {
 /* Score ([TUT] Figure 1 for one head; several weighted ReLU heads as read). */
 /* ------------------------------------------------------------------------ */
 
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+
 static double code_value(int dtype, const void* base, long idx) {
   if (dtype == ORC_BF16) return orc_bf16_value(((const uint16_t*)base)[idx]);
-  return orc_e4m3_value(((const uint8_t*)base)[idx]);
+  if (!e4m3_table_ready) {
+    for (int c = 0; c < 256; ++c) e4m3_table[c] = orc_e4m3_value((uint8_t)c);
+    e4m3_table_ready = 1;
+  }
+  return e4m3_table[((const uint8_t*)base)[idx]];
 }
 
 static const void* code_ptr(int dtype, const void* base, long idx) {
@@ -111,24 +118,54 @@ static const void* code_ptr(int dtype, const void* base, long idx) {
   return (const uint8_t*)base + idx;
 }
 
-/* S = sum_h w[h] * max(0, sum_d q[h][d] * k_s[d]).  For fp8 the values are
- * scale * e4m3(code); the positive per-token scales are taken out of the sums
- * (ReLU and the sums are positively homogeneous), which keeps the code dot
- * product exact in double: every code product is a multiple of 2^-18 below
- * 2^18, and D of them fit in 53 bits. */
-double orc_score(const orc_view* v, const void* qc, float qs, const float* w, int s) {
-  const int H = v->H, D = v->D;
-  const void* kc = code_ptr(v->dtype, v->k, (long)s * D);
+/* The n values denoted by the codes starting at base[idx]. */
+static void decode_codes(int dtype, const void* base, long idx, int n, double* out) {
+  for (int i = 0; i < n; ++i) out[i] = code_value(dtype, base, idx + i);
+}
+
+/* S = sum_h w[h] * max(0, sum_d q[h][d] * k_s[d]) on decoded values qd [H][D]
+ * and kd [D]; d ascending inside a head, then h ascending. */
+static double score_decoded(int H, int D, const double* qd, const float* w, const double* kd) {
   double total = 0.0;
   for (int h = 0; h < H; ++h) {
     double dot = 0.0;
-    for (int d = 0; d < D; ++d)
-      dot += code_value(v->dtype, qc, (long)h * D + d) * code_value(v->dtype, kc, d);
+    for (int d = 0; d < D; ++d) dot += qd[(long)h * D + d] * kd[d];
     double relu = dot > 0.0 ? dot : 0.0;
     total += (double)w[h] * relu;
   }
+  return total;
+}
+
+/* Score of the decoded query qd (scale qs, weights w) against key s.  For fp8
+ * the values are scale * e4m3(code); the positive per-token scales are taken
+ * out of the sums (ReLU and the sums are positively homogeneous), which keeps
+ * the code dot product exact in double: every code product is a multiple of
+ * 2^-18 below 2^18, and D of them fit in 53 bits. */
+static double score_key(const orc_view* v, const double* qd, float qs, const float* w, int s,
+                        double* kd) {
+  decode_codes(v->dtype, v->k, (long)s * v->D, v->D, kd);
+  double total = score_decoded(v->H, v->D, qd, w, kd);
   if (v->dtype == ORC_FP8_E4M3) total = total * (double)qs * (double)v->k_scale[s];
   return total;
+}
+
+/* Scores of one query (codes qc) against the listed keys (keys 0..n-1 when
+ * keys is NULL). */
+static void score_keys(const orc_view* v, const void* qc, float qs, const float* w,
+                       const int32_t* keys, int n, double* out) {
+  double* qd = (double*)malloc(sizeof(double) * (size_t)v->H * v->D);
+  double* kd = (double*)malloc(sizeof(double) * (size_t)v->D);
+  decode_codes(v->dtype, qc, 0, v->H * v->D, qd);
+  for (int i = 0; i < n; ++i) out[i] = score_key(v, qd, qs, w, keys ? keys[i] : i, kd);
+  free(qd);
+  free(kd);
+}
+
+double orc_score(const orc_view* v, const void* qc, float qs, const float* w, int s) {
+  double r;
+  int32_t key = s;
+  score_keys(v, qc, qs, w, &key, 1, &r);
+  return r;
 }
 
 static float row_scale(const orc_view* v, int row) {
@@ -137,15 +174,14 @@ static float row_scale(const orc_view* v, int row) {
 
 void orc_score_row(const orc_view* v, int row, int n, double* out) {
   const void* qc = code_ptr(v->dtype, v->q, (long)row * v->H * v->D);
-  const float* w = v->w + (long)row * v->H;
-  for (int s = 0; s < n; ++s) out[s] = orc_score(v, qc, row_scale(v, row), w, s);
+  score_keys(v, qc, row_scale(v, row), v->w + (long)row * v->H, NULL, n, out);
 }
 
 void orc_score_pairs(const orc_view* v, const int32_t* rows, const int32_t* keys, int npairs,
                      double* out) {
   for (int i = 0; i < npairs; ++i) {
     const void* qc = code_ptr(v->dtype, v->q, (long)rows[i] * v->H * v->D);
-    out[i] = orc_score(v, qc, row_scale(v, rows[i]), v->w + (long)rows[i] * v->H, keys[i]);
+    score_keys(v, qc, row_scale(v, rows[i]), v->w + (long)rows[i] * v->H, keys + i, 1, out + i);
   }
 }
 
@@ -188,8 +224,8 @@ void orc_topk(int n, const int32_t* pos, const double* score, int m, int32_t* ou
 }
 
 /* ------------------------------------------------------------------------ */
-/* Proxy query ([BLOG] proxy_q = mean(group); [ABS] "aggregates a group into  */
-/* a single proxy query").  Readings: the head weights are averaged the same */
+/* Proxy query ([BLOG] the proxy is the group mean; [ABS] one proxy query    */
+/* stands for the group).  Readings: the head weights are averaged the same  */
 /* way; the mean is taken in binary32, adding the members in ascending       */
 /* position and dividing by the member count; the result is rounded back to */
 /* the input type (bf16 round-to-nearest-even, or for fp8 a fresh per-proxy  */
@@ -278,10 +314,8 @@ void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, in
       double* sc = (double*)malloc(sizeof(double) * (size_t)(t + 1));
       int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(t + 1));
       const void* qc = code_ptr(v->dtype, v->q, (long)(row0 + i) * H * D);
-      for (int s = 0; s <= t; ++s) {
-        sc[s] = orc_score(v, qc, row_scale(v, row0 + i), v->w + (long)(row0 + i) * H, s);
-        pos[s] = s;
-      }
+      score_keys(v, qc, row_scale(v, row0 + i), v->w + (long)(row0 + i) * H, NULL, t + 1, sc);
+      for (int s = 0; s <= t; ++s) pos[s] = s;
       orc_topk(t + 1, pos, sc, topk, out + (long)i * topk);
       free(sc);
       free(pos);
@@ -297,10 +331,8 @@ void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, in
 
   double* psc = (double*)malloc(sizeof(double) * (size_t)nk);
   int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)nk);
-  for (int s = 0; s < nk; ++s) {
-    psc[s] = orc_score(v, pq, ps, pw, s);
-    pos[s] = s;
-  }
+  score_keys(v, pq, ps, pw, NULL, nk, psc);
+  for (int s = 0; s < nk; ++s) pos[s] = s;
   if (proxy_scores_out) memcpy(proxy_scores_out, psc, sizeof(double) * (size_t)nk);
 
   if (mode == ORC_REUSE) {
@@ -326,12 +358,9 @@ void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, in
       int t = pos0 + i;
       const void* qc = code_ptr(v->dtype, v->q, (long)(row0 + i) * H * D);
       int np = 0;
-      for (int j = 0; j < C; ++j) {
-        if (cand[j] < 0 || cand[j] > t) continue;
-        mpos[np] = cand[j];
-        msc[np] = orc_score(v, qc, row_scale(v, row0 + i), v->w + (long)(row0 + i) * H, cand[j]);
-        ++np;
-      }
+      for (int j = 0; j < C; ++j)
+        if (cand[j] >= 0 && cand[j] <= t) mpos[np++] = cand[j];
+      score_keys(v, qc, row_scale(v, row0 + i), v->w + (long)(row0 + i) * H, mpos, np, msc);
       orc_topk(np, mpos, msc, topk, out + (long)i * topk);
     }
     free(cand);

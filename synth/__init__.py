@@ -59,7 +59,7 @@ class PrefillInputs:
 class DecodeInputs:
     """One multi-token-prediction decode step over B cached sequences.
 
-    q: [B,g,H,D] codes of the g queries decoded together (positions n_b-g..n_b-1)
+    q: [B,g,H,D] codes of the g queries of one MTP step (positions n_b-g..n_b-1)
     q_scale: [B,g]; w: [B,g,H]; k: [B,Lmax,D] key cache codes; k_scale: [B,Lmax]
     cache_len: [B] int32 keys held per sequence, the g new keys included.
     """

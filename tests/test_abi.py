@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every function include/pivot.h declares, and
+rejects bad arguments on the host before anything is launched.  CPU only: the
+pointers below are never dereferenced because validation fails first."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import top_token_selection_pivot_amd as pv
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pivot.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_ALIGN, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
+FAKE = 0x100000  # aligned, never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pivot_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pv.library_path()):
+        from top_token_selection_pivot_amd import build
+        build.build(verbose=False)
+    return pv.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pivot_version() >= 100
+
+
+def _call(lib, **kw):
+    a = dict(q=FAKE, qs=None, w=FAKE, k=FAKE, ks=None, L=2048, H=4, D=32, g=4, topk=64, C=256,
+             mode=pv.REFINE, dtype=0, out=FAKE, ws=FAKE, wsb=1 << 40, st=None)
+    a.update(kw)
+    return lib.pivot_indexer(a["q"], a["qs"], a["w"], a["k"], a["ks"], a["L"], a["H"], a["D"],
+                             a["g"], a["topk"], a["C"], a["mode"], a["dtype"], a["out"], a["ws"],
+                             a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), ERR_NULL),
+    (dict(w=None), ERR_NULL),
+    (dict(out=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(dtype=1), ERR_NULL),               # fp8 without scales
+    (dict(H=0), ERR_SHAPE),
+    (dict(H=65), ERR_SHAPE),
+    (dict(D=48), ERR_SHAPE),
+    (dict(D=32, dtype=1, qs=FAKE, ks=FAKE), ERR_SHAPE),  # fp8 needs D in {64,128,256}
+    (dict(L=0), ERR_SHAPE),
+    (dict(g=0), ERR_PARAM),
+    (dict(topk=0), ERR_PARAM),
+    (dict(C=63), ERR_PARAM),                 # Refine needs C >= topk
+    (dict(mode=7), ERR_PARAM),
+    (dict(dtype=5), ERR_PARAM),
+    (dict(q=FAKE + 8), ERR_ALIGN),
+    (dict(k=FAKE + 4), ERR_ALIGN),
+    (dict(w=FAKE + 2), ERR_ALIGN),
+    (dict(ws=FAKE + 64), ERR_ALIGN),
+    (dict(wsb=1024), ERR_WORKSPACE),
+])
+def test_prefill_validation(lib, kw, status):
+    assert _call(lib, **kw) == status
+    assert lib.pivot_last_error()  # a message is recorded
+
+
+def test_reuse_ignores_C(lib):
+    # Reuse does not use C, so C < topk is fine: the call only fails on the workspace here
+    assert _call(lib, mode=pv.REUSE, C=0, wsb=16) == ERR_WORKSPACE
+
+
+def test_decode_validation(lib):
+    f = lib.pivot_indexer_decode
+    base = [FAKE, None, FAKE, FAKE, None, FAKE, 32, 131072, 64, 128, 2, 2048, 4096, pv.REFINE, 0,
+            FAKE, FAKE, 1 << 40, None]
+    def call(**kw):
+        a = list(base)
+        idx = dict(q=0, w=2, k=3, cl=5, B=6, Lmax=7, H=8, D=9, g=10, topk=11, C=12, mode=13,
+                   dtype=14, out=15, ws=16, wsb=17)
+        for k_, v in kw.items():
+            a[idx[k_]] = v
+        return f(*a)
+    assert call(cl=None) == ERR_NULL
+    assert call(B=0) == ERR_SHAPE
+    assert call(g=200000) == ERR_PARAM
+    assert call(C=100) == ERR_PARAM
+    assert call(wsb=100) == ERR_WORKSPACE
+    assert call(dtype=1) == ERR_NULL
+
+
+def test_workspace_sizes(lib):
+    # minimum <= preferred; both grow with L; Reuse needs less than Refine
+    for mode in (pv.DENSE, pv.REUSE, pv.REFINE):
+        mn = lib.pivot_workspace_min_size(131072, 64, 128, 8, 2048, 4096, mode, 0)
+        pf = lib.pivot_workspace_size(131072, 64, 128, 8, 2048, 4096, mode, 0)
+        assert 0 < mn <= pf
+    assert lib.pivot_workspace_size(0, 64, 128, 8, 2048, 4096, pv.REFINE, 0) == 0
+    assert (lib.pivot_workspace_size(16384, 64, 128, 8, 2048, 4096, pv.REUSE, 0)
+            < lib.pivot_workspace_size(16384, 64, 128, 8, 2048, 4096, pv.REFINE, 0))
+    assert lib.pivot_decode_workspace_size(32, 131072, 64, 128, 2, 2048, 4096, pv.REFINE, 1) > 32 * 131072 * 4
+
+
+def test_python_binding_fails_loudly_without_device():
+    import torch
+    q = torch.zeros((16, 4, 32), dtype=torch.bfloat16)
+    with pytest.raises(pv.PivotError):
+        pv.indexer(q, torch.zeros((16, 4)), torch.zeros((16, 32), dtype=torch.bfloat16), g=4,
+                   topk=4, C=8)

@@ -1,0 +1,264 @@
+"""GPU parity on integer-valued inputs: every binary32 sum is exact there, so the
+HIP path must reproduce the oracle's indices bit for bit.  Covers the
+matrix-core layout probe, the pages' worked example, the tiny prefill workload
+(L=2048, H=4, D=32, g=4, topk=64, C=256), proxy bits, candidate sets, edge
+cases (ragged groups, short rows, tiny and maximal shapes, chunked passes)
+and the decode grouping."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_token_selection_pivot_amd as pv
+from conftest import GOLDEN
+from parity import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, mode, g, topk, C, **kw):
+    d = to_device(inp)
+    out = pv.indexer(d["q"], d["w"], d["k"], g=g, topk=topk, C=C, mode=mode,
+                     q_scale=d["q_scale"], k_scale=d["k_scale"], **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _oracle_all(inp, mode, g, topk, C):
+    v = oracle.View.of(inp)
+    if mode == "dense":
+        return oracle.dense_rows(v, np.arange(inp.L), topk)
+    G = (inp.L + g - 1) // g
+    rows, _ = oracle.prefill_groups(v, inp.L, g, topk, C, mode, np.arange(G))
+    return rows
+
+
+def test_mfma_layout_selftest():
+    print("case: matrix-core layout probe", flush=True)
+    out = pv.selftest_mfma_layout().cpu().numpy()  # [probe][fmt][lane][acc]
+    lane = np.arange(64)[:, None]
+    i = np.arange(16)[None, :]
+    rows = 8 * (i // 4) + 4 * (lane // 32) + (i % 4)
+    cols = np.broadcast_to(lane % 32, (64, 16))
+    for f in (0, 1):
+        assert np.array_equal(out[0, f], rows), f"row layout, format {f}"
+        assert np.array_equal(out[1, f], cols), f"column layout, format {f}"
+        assert np.all(out[2, f] == 1), f"k-slice pairing, format {f}"
+
+
+def _pad_view(q, w, k, H=1, D=32):
+    """Zero-pad the pages' 2-d example to D=32 (zero padding leaves every score
+    unchanged)."""
+    L = q.shape[0]
+    qp = np.zeros((L, H, D), np.float32)
+    qp[:, :q.shape[1], :q.shape[2]] = q
+    kp = np.zeros((L, D), np.float32)
+    kp[:, :k.shape[1]] = k
+    return synth.PrefillInputs("bf16", L, H, D, synth.encode_bf16(qp), None,
+                               np.asarray(w, np.float32), synth.encode_bf16(kp), None)
+
+
+def test_worked_example_fig1():
+    print("case: worked example (Figure 1), dense top-3", flush=True)
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example_fig1.json")))
+    a = ex["keys_first_component"]
+    b = ex["keys_second_component_p0_to_p6"] + [ex["key_p7_second_component"]]
+    q = np.zeros((8, 1, 2), np.float32)
+    q[:, 0] = [1, 0]
+    q[6, 0] = ex["query_p6"]
+    q[7, 0] = ex["query_p7"]
+    inp = _pad_view(q, np.ones((8, 1)), np.stack([a, b], 1))
+    out = _run(inp, "dense", 1, 3, 3)
+    assert out[7].tolist() == ex["top3_p7"]
+    assert out[6].tolist() == ex["top3_p6"]
+
+
+def test_derived_pivot_example():
+    print("case: derived PIVOT example, g=2", flush=True)
+    ex = json.load(open(os.path.join(GOLDEN, "derived_pivot_example.json")))
+    q = np.zeros((8, 1, 2), np.float32)
+    q[:6, 0] = [[1, 0], [0, 1]] * 3
+    q[6, 0] = ex["q6"]
+    q[7, 0] = ex["q7"]
+    inp = _pad_view(q, np.ones((8, 1)), np.stack([ex["a"], ex["b"]], 1))
+    out = _run(inp, "reuse", 2, 3, 3)
+    assert out[6].tolist() == ex["reuse_k3"]["member6"]
+    assert out[7].tolist() == ex["reuse_k3"]["member7"]
+    out = _run(inp, "refine", 2, 3, 4)
+    assert out[6].tolist() == ex["refine_k3_C4"]["member6"]
+    assert out[7].tolist() == ex["refine_k3_C4"]["member7"]
+    out = _run(inp, "refine", 2, 3, 8)
+    assert out[6].tolist() == ex["refine_k3_C8"]["member6"]
+    assert out[7].tolist() == ex["refine_k3_C8"]["member7"]
+    # every row, against the oracle
+    for mode, C_ in (("reuse", 3), ("refine", 4), ("refine", 8), ("dense", 3)):
+        assert np.array_equal(_run(inp, mode, 2, 3, C_), _oracle_all(inp, mode, 2, 3, C_))
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return synth.make("tiny_prefill_2k")
+
+
+@pytest.mark.parametrize("mode", ["dense", "reuse", "refine"])
+def test_tiny_prefill_bit_exact(tiny, mode):
+    print(f"case: tiny prefill L=2048 H=4 D=32 g=4 k=64 C=256 {mode}", flush=True)
+    got = _run(tiny, mode, 4, 64, 256)
+    ref = _oracle_all(tiny, mode, 4, 64, 256)
+    assert np.array_equal(got, ref)
+
+
+def test_tiny_proxy_bits_and_candidates(tiny):
+    print("case: tiny prefill proxy bits and candidate sets", flush=True)
+    d = to_device(tiny)
+    v = oracle.View.of(tiny)
+    for g in (4, 3, 16):
+        qbar, qs, wbar = pv.proxy_mean(d["q"], d["w"], g)
+        qbar = qbar.view(torch.int16).cpu().numpy().view(np.uint16)
+        qs, wbar = qs.cpu().numpy(), wbar.cpu().numpy()
+        for j in list(range(0, 2048 // g, 37)) + [(2048 + g - 1) // g - 1]:
+            n = min(g, 2048 - j * g)
+            c, s, wb = oracle.proxy(v, j * g, n)
+            assert np.array_equal(qbar[j], c) and qs[j] == s and np.array_equal(wbar[j], wb)
+    for mode, m in (("refine", 256), ("reuse", 64)):
+        cand = pv.candidates(d["q"], d["w"], d["k"], g=4, topk=64, C=256, mode=mode).cpu().numpy()
+        _, ref = oracle.prefill_groups(v, 2048, 4, 64, 256, mode, np.arange(512))
+        assert np.array_equal(cand, ref)
+
+
+def test_fp8_proxy_bits():
+    print("case: fp8 proxy bits (float inputs, partial last group)", flush=True)
+    inp = synth.dsa_prefill(L=203, H=64, D=128, dtype="fp8", seed=77)
+    d = to_device(inp)
+    v = oracle.View.of(inp)
+    for g in (8, 2, 1):
+        qbar, qs, wbar = pv.proxy_mean(d["q"], d["w"], g, q_scale=d["q_scale"])
+        qbar, qs, wbar = qbar.cpu().numpy(), qs.cpu().numpy(), wbar.cpu().numpy()
+        for j in range((203 + g - 1) // g):
+            n = min(g, 203 - j * g)
+            c, s, wb = oracle.proxy(v, j * g, n)
+            assert np.array_equal(qbar[j], c), (g, j)
+            assert qs[j] == s and np.array_equal(wbar[j], wb), (g, j)
+
+
+SHAPES = [  # (L, H, D, g, topk, C, dtype)
+    (1, 4, 32, 4, 8, 16, "bf16"),        # a single query
+    (50, 4, 32, 8, 64, 64, "bf16"),       # every row shorter than topk
+    (1003, 64, 128, 8, 96, 200, "bf16"),  # partial last group, ragged tiles
+    (2049, 33, 64, 16, 128, 256, "bf16"), # ragged key chunk, odd head count
+    (10, 2, 32, 16, 3, 5, "bf16"),        # g larger than L
+    (700, 1, 256, 5, 40, 80, "bf16"),     # one head, widest D, odd g
+    (777, 64, 128, 1, 50, 50, "bf16"),    # g = 1
+    (640, 48, 64, 4, 32, 32, "fp8"),      # fp8 codes, C = topk
+    (901, 64, 128, 1, 64, 96, "fp8"),
+    (300, 7, 256, 3, 17, 40, "fp8"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "L{}H{}D{}g{}k{}C{}{}".format(*s))
+def test_shapes_exact(shape):
+    L, H, D, g, topk, C_, dt = shape
+    print(f"case: exact shape {shape}", flush=True)
+    inp = synth.small_integer(L, H, D, seed=L + H + D, qmax=2, kmax=2, wmax=3, dtype=dt)
+    modes = ["dense", "reuse", "refine"]
+    if dt == "fp8":
+        # binary32 sums of fp8 integer codes are exact only without the proxy
+        # re-quantisation, i.e. for the dense indexer and one-member groups
+        modes = ["dense"] + (["reuse", "refine"] if g == 1 else [])
+    for mode in modes:
+        got = _run(inp, mode, g, topk, C_)
+        ref = _oracle_all(inp, mode, g, topk, C_)
+        assert np.array_equal(got, ref), mode
+
+
+def test_identities_on_gpu():
+    print("case: GPU identities (Refine g=1 / C>=L == dense, C=k Refine == Reuse)", flush=True)
+    inp = synth.small_integer(1500, 64, 128, seed=9, qmax=2, kmax=2, wmax=3)
+    dense = _run(inp, "dense", 1, 100, 100)
+    assert np.array_equal(_run(inp, "refine", 1, 100, 100), dense)
+    assert np.array_equal(_run(inp, "refine", 8, 100, 1500), dense)
+    assert np.array_equal(_run(inp, "reuse", 1, 100, 100), dense)
+    assert np.array_equal(_run(inp, "refine", 8, 100, 100), _run(inp, "reuse", 8, 100, 100))
+
+
+def test_chunked_passes_match_single_pass():
+    print("case: minimum workspace (many passes) vs default", flush=True)
+    inp = synth.small_integer(3000, 64, 128, seed=4, qmax=2, kmax=2, wmax=3)
+    d = to_device(inp)
+    for mode in ("dense", "reuse", "refine"):
+        big = _run(inp, mode, 8, 128, 256)
+        nmin = pv.load().pivot_workspace_min_size(3000, 64, 128, 8, 128, 256, pv._mode(mode), 0)
+        ws = torch.empty(nmin, dtype=torch.uint8, device="cuda")
+        small = pv.indexer(d["q"], d["w"], d["k"], g=8, topk=128, C=256, mode=mode,
+                           workspace=ws).cpu().numpy()
+        assert np.array_equal(big, small), mode
+
+
+def test_deterministic_repeat():
+    print("case: repeated calls are identical", flush=True)
+    inp = synth.dsa_prefill(L=4096, H=64, D=128, seed=12)
+    a = _run(inp, "refine", 8, 256, 512)
+    b = _run(inp, "refine", 8, 256, 512)
+    assert np.array_equal(a, b)
+
+
+def _decode_inputs(B, lens, g, H=8, D=64, dtype="bf16", Lmax=None, seed=3):
+    Lmax = Lmax or max(lens)
+    rng = np.random.default_rng(seed)
+    qf = rng.integers(-2, 3, (B, g, H, D)).astype(np.float32)
+    kf = rng.integers(-2, 3, (B, Lmax, D)).astype(np.float32)
+    w = rng.integers(1, 4, (B, g, H)).astype(np.float32)
+    if dtype == "bf16":
+        return synth.DecodeInputs("bf16", B, Lmax, H, D, g, synth.encode_bf16(qf), None, w,
+                                  synth.encode_bf16(kf), None, np.asarray(lens, np.int32))
+    return synth.DecodeInputs("fp8", B, Lmax, H, D, g, synth._encode_fp8(qf),
+                              np.ones((B, g), np.float32), w, synth._encode_fp8(kf),
+                              np.ones((B, Lmax), np.float32), np.asarray(lens, np.int32))
+
+
+@pytest.mark.parametrize("mode", ["dense", "reuse", "refine"])
+def test_decode_exact(mode):
+    print(f"case: decode exact B=5 g=2 {mode}", flush=True)
+    lens = [2, 37, 1000, 999, 1500]
+    dec = _decode_inputs(5, lens, g=2, H=8, D=64, Lmax=1500)
+    d = to_device(dec)
+    out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=40, C=100,
+                            mode=mode).cpu().numpy()
+    for b in range(5):
+        ref, _, _ = oracle.decode_seq(dec, b, 40, 100, mode)
+        assert np.array_equal(out[b], ref), b
+
+
+def test_decode_matches_last_prefill_group_and_rejects_bad_lengths():
+    print("case: decode == last prefill group; invalid cache lengths give -1 rows", flush=True)
+    g = 4
+    inp = synth.small_integer(400, 16, 64, seed=8, qmax=2, kmax=2, wmax=3)
+    pre = _run(inp, "refine", g, 30, 60)
+    dec = synth.DecodeInputs("bf16", 1, 400, 16, 64, g, inp.q[None, -g:], None,
+                             inp.w[None, -g:], inp.k[None], None, np.array([400], np.int32))
+    d = to_device(dec)
+    out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=30, C=60,
+                            mode="refine").cpu().numpy()
+    assert np.array_equal(out[0], pre[-g:])
+    bad = _decode_inputs(3, [1, 0, 70], g=2, H=4, D=32, Lmax=64)
+    d = to_device(bad)
+    d["cache_len"] = torch.tensor([1, 0, 70], dtype=torch.int32, device="cuda")
+    for mode in ("dense", "reuse", "refine"):
+        out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=8, C=16,
+                                mode=mode).cpu().numpy()
+        assert np.all(out == -1), mode
+
+
+def test_decode_fp8_exact_dense():
+    print("case: decode fp8 integer codes, dense", flush=True)
+    dec = _decode_inputs(4, [64, 500, 2000, 3], g=3, H=64, D=128, dtype="fp8", Lmax=2000)
+    d = to_device(dec)
+    out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=50, C=50, mode="dense",
+                            q_scale=d["q_scale"], k_scale=d["k_scale"]).cpu().numpy()
+    for b in range(4):
+        ref, _, _ = oracle.decode_seq(dec, b, 50, 50, "dense")
+        assert np.array_equal(out[b], ref), b

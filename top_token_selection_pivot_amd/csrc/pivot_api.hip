@@ -1,0 +1,544 @@
+// pivot_api.hip -- C ABI of the PIVOT indexer (declared in include/pivot.h):
+// argument validation, workspace planning and the sequence of kernel launches
+// on the caller's stream.  No device memory is allocated here.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/pivot.h"
+#include "pivot_kernels.h"
+
+using namespace pivot;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+constexpr size_t kAlign = 256;
+constexpr size_t kScoreBudget = size_t(1) << 30;  // preferred score bytes per pass
+constexpr int kScanKeyChunk = 2048;              // keys per scan workgroup
+constexpr int kDecodeKeyChunk = 1024;            // keys per decode-scan workgroup
+constexpr int kRefineSlotChunk = 1024;           // candidate slots per refine workgroup
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int esize(int dtype) { return dtype == PIVOT_BF16 ? 2 : 1; }
+
+// ---------------------------------------------------------------------------
+// Prefill plan.  Rows are proxies (REUSE/REFINE, one per group) or queries
+// (DENSE).  Score rows of one pass live in one region, reused by the Refine
+// member scores of the same pass.
+// ---------------------------------------------------------------------------
+struct PrefillPlan {
+  int G;           // groups (= L for DENSE)
+  int m;           // proxy selection size: C (REFINE) or topk
+  long long ldS;   // score row stride (floats)
+  long long ldR;   // refine member row stride (floats)
+  size_t off_qbar, off_qs, off_wbar, off_cand, off_S;
+  size_t per_row;  // bytes of score region per row (group)
+  size_t fixed;    // bytes before the chunked part
+  size_t per_chunk_row;
+};
+
+PrefillPlan plan_prefill(int L, int H, int D, int g, int topk, int C, int mode, int dtype) {
+  PrefillPlan p{};
+  const bool dense = mode == PIVOT_MODE_DENSE;
+  p.G = dense ? L : (L + g - 1) / g;
+  p.m = mode == PIVOT_MODE_REFINE ? C : topk;
+  p.ldS = round_up(L, 64);
+  p.ldR = round_up(C, 64);
+  size_t off = 0;
+  if (!dense) {
+    p.off_qbar = off;
+    off = align_up(off + (size_t)p.G * H * D * esize(dtype));
+    p.off_qs = off;
+    off = align_up(off + (size_t)p.G * 4);
+    p.off_wbar = off;
+    off = align_up(off + (size_t)p.G * H * 4);
+  }
+  p.fixed = off;
+  size_t srow = (size_t)p.ldS * 4;
+  if (mode == PIVOT_MODE_REFINE) srow = std::max(srow, (size_t)g * (size_t)p.ldR * 4);
+  p.per_row = srow;
+  p.per_chunk_row = srow + (dense ? 0 : (size_t)p.m * 4);
+  return p;
+}
+
+// Workspace bytes for `rows` rows per pass.
+size_t prefill_bytes(const PrefillPlan& p, int rows, bool dense) {
+  size_t cand = dense ? 0 : align_up((size_t)rows * p.m * 4);
+  return p.fixed + cand + align_up((size_t)rows * p.per_row) + kAlign;
+}
+
+int chunk_rows_for(const PrefillPlan& p, size_t ws, bool dense) {
+  // largest multiple of 8 rows (or all rows) that fits
+  if (prefill_bytes(p, p.G, dense) <= ws) return p.G;
+  if (ws < p.fixed + 3 * kAlign) return 0;
+  long long rows = (long long)((ws - p.fixed - 3 * kAlign) / p.per_chunk_row);
+  rows = rows / 8 * 8;
+  while (rows > 0 && prefill_bytes(p, (int)rows, dense) > ws) rows -= 8;
+  return (int)std::min<long long>(rows, p.G);
+}
+
+int validate_common(const void* q, const float* q_scale, const float* w, const void* k,
+                    const float* k_scale, int H, int D, int g, int topk, int C, int mode,
+                    int dtype) {
+  if (dtype != PIVOT_BF16 && dtype != PIVOT_FP8_E4M3)
+    return fail(PIVOT_ERR_PARAM, "dtype %d is not PIVOT_BF16 or PIVOT_FP8_E4M3", dtype);
+  if (mode != PIVOT_MODE_DENSE && mode != PIVOT_MODE_REUSE && mode != PIVOT_MODE_REFINE)
+    return fail(PIVOT_ERR_PARAM, "mode %d is not DENSE, REUSE or REFINE", mode);
+  if (!q || !w || !k) return fail(PIVOT_ERR_NULL, "q, w and k must be non-NULL");
+  if (dtype == PIVOT_FP8_E4M3 && (!q_scale || !k_scale))
+    return fail(PIVOT_ERR_NULL, "fp8 inputs need q_scale and k_scale");
+  if (H < 1 || H > 64) return fail(PIVOT_ERR_SHAPE, "H=%d outside 1..64", H);
+  if (!score_shape_supported(dtype, D))
+    return fail(PIVOT_ERR_SHAPE, "D=%d unsupported for %s", D, dtype == PIVOT_BF16 ? "bf16" : "fp8");
+  if (g < 1) return fail(PIVOT_ERR_PARAM, "g=%d must be >= 1", g);
+  if (topk < 1) return fail(PIVOT_ERR_PARAM, "topk=%d must be >= 1", topk);
+  if (mode == PIVOT_MODE_REFINE && C < topk)
+    return fail(PIVOT_ERR_PARAM, "Refine needs C >= topk (C=%d, topk=%d)", C, topk);
+  if (!aligned(q, 16) || !aligned(k, 16)) return fail(PIVOT_ERR_ALIGN, "q and k must be 16-byte aligned");
+  if (!aligned(w, 4) || (q_scale && !aligned(q_scale, 4)) || (k_scale && !aligned(k_scale, 4)))
+    return fail(PIVOT_ERR_ALIGN, "w and scales must be 4-byte aligned");
+  return PIVOT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PIVOT_OK;
+  return fail(PIVOT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Optional per-launch event timing (pivot_profile_enable).
+struct TimedLaunch {
+  int cls;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<TimedLaunch> g_prof;
+
+struct ProfileScope {
+  hipStream_t st;
+  int cls;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfileScope(int cls_, hipStream_t st_) : st(st_), cls(cls_) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    if (hipEventCreate(&a) != hipSuccess) {
+      a = nullptr;
+      return;
+    }
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      a = nullptr;
+      return;
+    }
+    if (hipEventRecord(a, st) != hipSuccess) drop();
+  }
+  void drop() {
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    a = b = nullptr;
+  }
+  ~ProfileScope() {
+    if (!a) return;
+    if (hipEventRecord(b, st) != hipSuccess) {
+      drop();
+      return;
+    }
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({cls, a, b});
+  }
+};
+
+#define PIVOT_LAUNCH_K(cls, st, expr, what)           \
+  do {                                                \
+    ProfileScope prof_(cls, st);                      \
+    int st_ = hip_status((expr), what);               \
+    if (st_ != PIVOT_OK) return st_;                  \
+  } while (0)
+
+#define PIVOT_LAUNCH(expr, what)                      \
+  do {                                                \
+    int st_ = hip_status((expr), what);               \
+    if (st_ != PIVOT_OK) return st_;                  \
+  } while (0)
+
+// Runs the prefill path.  `cand_user` (optional) receives every group's top-m
+// and skips the member step (pivot_candidates).
+int run_prefill(const void* q, const float* q_scale, const float* w, const void* k,
+                const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
+                int dtype, int32_t* out, int32_t* cand_user, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = validate_common(q, q_scale, w, k, k_scale, H, D, g, topk, C, mode, dtype);
+  if (st) return st;
+  if (L < 1) return fail(PIVOT_ERR_SHAPE, "L=%d must be >= 1", L);
+  if ((long long)L * H * D > (1ll << 40)) return fail(PIVOT_ERR_SHAPE, "L*H*D too large");
+  if (!out && !cand_user) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  if ((out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)))
+    return fail(PIVOT_ERR_ALIGN, "output must be 4-byte aligned");
+  if (!workspace) return fail(PIVOT_ERR_NULL, "workspace must be non-NULL");
+  if (!aligned(workspace, kAlign)) return fail(PIVOT_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const bool dense = mode == PIVOT_MODE_DENSE;
+  if (dense) g = 1;
+  const PrefillPlan p = plan_prefill(L, H, D, g, topk, C, mode, dtype);
+  const int CR = chunk_rows_for(p, workspace_bytes, dense);
+  if (CR <= 0)
+    return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", workspace_bytes,
+                prefill_bytes(p, std::min(p.G, 8), dense));
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* qbar = ws + p.off_qbar;
+  float* qbs = (float*)(ws + p.off_qs);
+  float* wbar = (float*)(ws + p.off_wbar);
+  int32_t* cand = (int32_t*)(ws + p.fixed);
+  float* S = (float*)(ws + p.fixed + (dense ? 0 : align_up((size_t)CR * p.m * 4)));
+  const uint8_t* qb = (const uint8_t*)q;
+  const uint8_t* kb = (const uint8_t*)k;
+
+  if (!dense) {
+    ProxyArgs pa{qb, q_scale, w, L, H, D, g, qbar, qbs, wbar};
+    PIVOT_LAUNCH_K(PIVOT_K_PROXY, s, launch_proxy_mean(pa, dtype, s), "proxy mean");
+  }
+  for (int r0 = 0; r0 < p.G; r0 += CR) {
+    const int r1 = std::min(p.G, r0 + CR);
+    ScanArgs sa{};
+    if (dense) {
+      sa = ScanArgs{qb, q_scale, w, kb, k_scale, L, H, r0, r1, 1, 0, L - 1, kScanKeyChunk, S, p.ldS};
+    } else {
+      sa = ScanArgs{qbar, qbs, wbar, kb, k_scale, L, H, r0, r1, g, g - 1, L - 1, kScanKeyChunk, S,
+                    p.ldS};
+    }
+    PIVOT_LAUNCH_K(PIVOT_K_SCAN, s, launch_scan(sa, dtype, D, s), "scan");
+    TopkArgs ta{};
+    ta.S = S;
+    ta.ldS = p.ldS;
+    ta.row_begin = r0;
+    ta.nrows = r1 - r0;
+    ta.kind = kLenPos;
+    ta.pos_mul = dense ? 1 : g;
+    ta.pos_add = dense ? 0 : g - 1;
+    ta.pos_cap = L - 1;
+    if (dense) {
+      ta.m = topk;
+      ta.out = out + (size_t)r0 * topk;
+      ta.ldo = topk;
+      PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "dense top-k");
+      continue;
+    }
+    int32_t* cdst = cand_user ? cand_user + (size_t)r0 * p.m : cand;
+    ta.m = p.m;
+    ta.out = cdst;
+    ta.ldo = p.m;
+    PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "proxy top-m");
+    if (cand_user) continue;
+    const int row_begin = r0 * g, row_end = std::min(L, r1 * g);
+    if (mode == PIVOT_MODE_REUSE) {
+      BroadcastArgs ba{cdst, p.m, r0, out + (size_t)row_begin * topk, topk, 0, g, 0, nullptr,
+                       row_begin, row_end};
+      PIVOT_LAUNCH_K(PIVOT_K_BROADCAST, s, launch_broadcast(ba, s), "reuse broadcast");
+    } else {
+      RefineArgs ra{qb, q_scale, w, kb, k_scale, H, 0, L, g, 0, nullptr, r0, r1, cdst, p.m, p.m,
+                    kRefineSlotChunk, S, p.ldR, row_begin};
+      PIVOT_LAUNCH_K(PIVOT_K_REFINE, s, launch_refine(ra, dtype, D, s), "refine score");
+      TopkArgs tr{};
+      tr.S = S;
+      tr.ldS = p.ldR;
+      tr.row_begin = row_begin;
+      tr.nrows = row_end - row_begin;
+      tr.m = topk;
+      tr.out = out + (size_t)row_begin * topk;
+      tr.ldo = topk;
+      tr.kind = kLenRefine;
+      tr.decode = 0;
+      tr.g = g;
+      tr.map = cdst;
+      tr.ldmap = p.m;
+      tr.map_grp_begin = r0;
+      PIVOT_LAUNCH_K(PIVOT_K_MEMBER_SELECT, s, launch_topk(tr, s), "refine top-k");
+    }
+  }
+  return PIVOT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Decode plan.
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int m;
+  long long ldS, ldR;
+  size_t off_qbar, off_qs, off_wbar, off_cand, off_S, off_R, total;
+};
+
+DecodePlan plan_decode(int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                       int dtype) {
+  DecodePlan p{};
+  const bool dense = mode == PIVOT_MODE_DENSE;
+  p.m = mode == PIVOT_MODE_REFINE ? C : topk;
+  p.ldS = round_up(Lmax, 64);
+  p.ldR = round_up(C, 64);
+  size_t off = 0;
+  p.off_qbar = off;
+  if (!dense) off = align_up(off + (size_t)B * H * D * esize(dtype));
+  p.off_qs = off;
+  if (!dense) off = align_up(off + (size_t)B * 4);
+  p.off_wbar = off;
+  if (!dense) off = align_up(off + (size_t)B * H * 4);
+  p.off_cand = off;
+  if (!dense) off = align_up(off + (size_t)B * p.m * 4);
+  p.off_S = off;
+  off = align_up(off + (size_t)B * (dense ? g : 1) * p.ldS * 4);
+  p.off_R = off;
+  if (mode == PIVOT_MODE_REFINE) off = align_up(off + (size_t)B * g * p.ldR * 4);
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pivot_version(void) { return 100; }
+
+const char* pivot_status_string(int status) {
+  switch (status) {
+    case PIVOT_OK: return "ok";
+    case PIVOT_ERR_NULL: return "null pointer";
+    case PIVOT_ERR_SHAPE: return "unsupported shape";
+    case PIVOT_ERR_PARAM: return "invalid parameter";
+    case PIVOT_ERR_ALIGN: return "misaligned pointer";
+    case PIVOT_ERR_WORKSPACE: return "workspace too small";
+    case PIVOT_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* pivot_last_error(void) { return g_err; }
+
+size_t pivot_workspace_size(int L, int H, int D, int g, int topk, int C, int mode, int dtype) {
+  if (L < 1 || H < 1 || D < 1 || g < 1 || topk < 1) return 0;
+  const bool dense = mode == PIVOT_MODE_DENSE;
+  if (dense) g = 1;
+  const PrefillPlan p = plan_prefill(L, H, D, g, topk, C, mode, dtype);
+  long long rows = std::max<long long>(8, (long long)(kScoreBudget / p.per_row) / 8 * 8);
+  rows = std::min<long long>(rows, p.G);
+  return prefill_bytes(p, (int)rows, dense);
+}
+
+size_t pivot_workspace_min_size(int L, int H, int D, int g, int topk, int C, int mode, int dtype) {
+  if (L < 1 || H < 1 || D < 1 || g < 1 || topk < 1) return 0;
+  const bool dense = mode == PIVOT_MODE_DENSE;
+  if (dense) g = 1;
+  const PrefillPlan p = plan_prefill(L, H, D, g, topk, C, mode, dtype);
+  return prefill_bytes(p, std::min(p.G, 8), dense);
+}
+
+int pivot_indexer(const void* q, const float* q_scale, const float* w, const void* k,
+                  const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
+                  int dtype, int32_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  return run_prefill(q, q_scale, w, k, k_scale, L, H, D, g, topk, C, mode, dtype, out, nullptr,
+                     workspace, workspace_bytes, stream);
+}
+
+int pivot_candidates(const void* q, const float* q_scale, const float* w, const void* k,
+                     const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
+                     int dtype, int32_t* cand, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (mode == PIVOT_MODE_DENSE)
+    return fail(PIVOT_ERR_PARAM, "pivot_candidates needs mode REUSE or REFINE");
+  if (!cand) return fail(PIVOT_ERR_NULL, "cand must be non-NULL");
+  return run_prefill(q, q_scale, w, k, k_scale, L, H, D, g, topk, C, mode, dtype, nullptr, cand,
+                     workspace, workspace_bytes, stream);
+}
+
+int pivot_proxy_mean(const void* q, const float* q_scale, const float* w, int L, int H, int D,
+                     int g, int dtype, void* qbar, float* qbar_scale, float* wbar, void* stream) {
+  int st = validate_common(q, q_scale, w, q, q_scale, H, D, g, 1, 1, PIVOT_MODE_REUSE, dtype);
+  if (st) return st;
+  if (L < 1) return fail(PIVOT_ERR_SHAPE, "L=%d must be >= 1", L);
+  if (!qbar || !qbar_scale || !wbar) return fail(PIVOT_ERR_NULL, "qbar, qbar_scale and wbar must be non-NULL");
+  if (!aligned(qbar, 16) || !aligned(qbar_scale, 4) || !aligned(wbar, 4))
+    return fail(PIVOT_ERR_ALIGN, "qbar must be 16-byte aligned, qbar_scale and wbar 4-byte aligned");
+  ProxyArgs pa{(const uint8_t*)q, q_scale, w, L, H, D, g, (uint8_t*)qbar, qbar_scale, wbar};
+  PIVOT_LAUNCH(launch_proxy_mean(pa, dtype, (hipStream_t)stream), "proxy mean");
+  return PIVOT_OK;
+}
+
+size_t pivot_decode_workspace_size(int B, int Lmax, int H, int D, int g, int topk, int C,
+                                   int mode, int dtype) {
+  if (B < 1 || Lmax < 1 || H < 1 || D < 1 || g < 1 || topk < 1) return 0;
+  return plan_decode(B, Lmax, H, D, g, topk, C, mode, dtype).total + kAlign;
+}
+
+static int run_decode(const void* q, const float* q_scale, const float* w,
+                      const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                      int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                      int dtype, int32_t* out, int32_t* cand_user, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = validate_common(q, q_scale, w, k_cache, k_scale, H, D, g, topk, C, mode, dtype);
+  if (st) return st;
+  if (B < 1 || Lmax < 1) return fail(PIVOT_ERR_SHAPE, "B=%d and Lmax=%d must be >= 1", B, Lmax);
+  if (g > Lmax) return fail(PIVOT_ERR_PARAM, "g=%d exceeds Lmax=%d", g, Lmax);
+  if ((long long)B * Lmax * D > (1ll << 40)) return fail(PIVOT_ERR_SHAPE, "B*Lmax*D too large");
+  if (!cache_len || (!out && !cand_user) || !workspace)
+    return fail(PIVOT_ERR_NULL, "cache_len, out and workspace must be non-NULL");
+  if (!aligned(cache_len, 4) || (out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)))
+    return fail(PIVOT_ERR_ALIGN, "cache_len and outputs must be 4-byte aligned");
+  if (!aligned(workspace, kAlign)) return fail(PIVOT_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const DecodePlan p = plan_decode(B, Lmax, H, D, g, topk, C, mode, dtype);
+  if (workspace_bytes < p.total)
+    return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", workspace_bytes, p.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  const uint8_t* qb = (const uint8_t*)q;
+  const uint8_t* kb = (const uint8_t*)k_cache;
+  float* S = (float*)(ws + p.off_S);
+
+  if (mode == PIVOT_MODE_DENSE) {
+    DecScanArgs da{qb, q_scale, w, kb, k_scale, Lmax, H, cache_len, g, g, kDecodeKeyChunk, S, p.ldS};
+    PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, B, s), "decode scan");
+    TopkArgs ta{};
+    ta.S = S;
+    ta.ldS = p.ldS;
+    ta.row_begin = 0;
+    ta.nrows = B * g;
+    ta.m = topk;
+    ta.out = out;
+    ta.ldo = topk;
+    ta.kind = kLenDecodeDense;
+    ta.g = g;
+    ta.Lmax = Lmax;
+    ta.cache_len = cache_len;
+    PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "decode dense top-k");
+    return PIVOT_OK;
+  }
+  uint8_t* qbar = ws + p.off_qbar;
+  float* qbs = (float*)(ws + p.off_qs);
+  float* wbar = (float*)(ws + p.off_wbar);
+  int32_t* cand = cand_user ? cand_user : (int32_t*)(ws + p.off_cand);
+  ProxyArgs pa{qb, q_scale, w, B * g, H, D, g, qbar, qbs, wbar};
+  PIVOT_LAUNCH_K(PIVOT_K_PROXY, s, launch_proxy_mean(pa, dtype, s), "decode proxy mean");
+  DecScanArgs da{qbar, qbs, wbar, kb, k_scale, Lmax, H, cache_len, g, 1, kDecodeKeyChunk, S, p.ldS};
+  PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, B, s), "decode scan");
+  TopkArgs ta{};
+  ta.S = S;
+  ta.ldS = p.ldS;
+  ta.row_begin = 0;
+  ta.nrows = B;
+  ta.m = p.m;
+  ta.out = cand;
+  ta.ldo = p.m;
+  ta.kind = kLenCache;
+  ta.g = g;
+  ta.Lmax = Lmax;
+  ta.cache_len = cache_len;
+  PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "decode proxy top-m");
+  if (cand_user) return PIVOT_OK;
+  if (mode == PIVOT_MODE_REUSE) {
+    BroadcastArgs ba{cand, p.m, 0, out, topk, 1, g, Lmax, cache_len, 0, B * g};
+    PIVOT_LAUNCH_K(PIVOT_K_BROADCAST, s, launch_broadcast(ba, s), "decode reuse broadcast");
+    return PIVOT_OK;
+  }
+  float* R = (float*)(ws + p.off_R);
+  RefineArgs ra{qb, q_scale, w, kb, k_scale, H, 1, 0, g, Lmax, cache_len, 0, B, cand, p.m, p.m,
+                kRefineSlotChunk, R, p.ldR, 0};
+  PIVOT_LAUNCH_K(PIVOT_K_REFINE, s, launch_refine(ra, dtype, D, s), "decode refine score");
+  TopkArgs tr{};
+  tr.S = R;
+  tr.ldS = p.ldR;
+  tr.row_begin = 0;
+  tr.nrows = B * g;
+  tr.m = topk;
+  tr.out = out;
+  tr.ldo = topk;
+  tr.kind = kLenRefine;
+  tr.decode = 1;
+  tr.g = g;
+  tr.Lmax = Lmax;
+  tr.cache_len = cache_len;
+  tr.map = cand;
+  tr.ldmap = p.m;
+  tr.map_grp_begin = 0;
+  PIVOT_LAUNCH_K(PIVOT_K_MEMBER_SELECT, s, launch_topk(tr, s), "decode refine top-k");
+  return PIVOT_OK;
+}
+
+int pivot_indexer_decode(const void* q, const float* q_scale, const float* w,
+                         const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                         int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                         int dtype, int32_t* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  return run_decode(q, q_scale, w, k_cache, k_scale, cache_len, B, Lmax, H, D, g, topk, C, mode,
+                    dtype, out, nullptr, workspace, workspace_bytes, stream);
+}
+
+int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,
+                            const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                            int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                            int dtype, int32_t* cand, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (mode == PIVOT_MODE_DENSE)
+    return fail(PIVOT_ERR_PARAM, "pivot_decode_candidates needs mode REUSE or REFINE");
+  if (!cand) return fail(PIVOT_ERR_NULL, "cand must be non-NULL");
+  return run_decode(q, q_scale, w, k_cache, k_scale, cache_len, B, Lmax, H, D, g, topk, C, mode,
+                    dtype, nullptr, cand, workspace, workspace_bytes, stream);
+}
+
+int pivot_profile_enable(int on) {
+  g_prof_on.store(on != 0);
+  return PIVOT_OK;
+}
+
+int pivot_profile_read(double* ms, long long* launches, int n) {
+  if ((!ms || !launches) && n > 0) return fail(PIVOT_ERR_NULL, "ms and launches must be non-NULL");
+  for (int i = 0; i < n; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  std::vector<TimedLaunch> rec;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    rec.swap(g_prof);
+  }
+  int st = PIVOT_OK;
+  for (const TimedLaunch& t : rec) {
+    float el = 0.f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&el, t.start, t.stop);
+    if (e != hipSuccess && st == PIVOT_OK) st = hip_status(e, "profile read");
+    if (t.cls < n) {
+      ms[t.cls] += el;
+      launches[t.cls] += 1;
+    }
+    (void)hipEventDestroy(t.start);
+    (void)hipEventDestroy(t.stop);
+  }
+  return st;
+}
+
+int pivot_selftest_mfma_layout(int32_t* out, void* stream) {
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  PIVOT_LAUNCH(launch_selftest_mfma(out, (hipStream_t)stream), "mfma self-test");
+  return PIVOT_OK;
+}
+
+}  // extern "C"

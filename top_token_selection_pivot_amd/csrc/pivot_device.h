@@ -1,0 +1,182 @@
+// pivot_device.h -- device-side building blocks of the PIVOT indexer kernels
+// (gfx950 / CDNA4, wave64).
+//
+// Score tiles use the 32x32 matrix-core instructions with the H indexer heads
+// on the M axis and 32 keys on the N axis, so after the contraction over D each
+// lane holds one key column and half of the heads' dot products.  The head
+// reduction S = sum_h w[h] * max(0, dot_h) then runs inside the lane, with one
+// swap across the two lane halves at the end, and never leaves registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pivot {
+
+enum : int { kBF16 = 0, kFP8 = 1 };
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kTileN = 32;  // keys per matrix-core tile
+
+// ---------------------------------------------------------------------------
+// Operand formats.  A "fragment" is what one lane feeds one 32x32 instruction
+// for one operand.  Lane l covers row/column (l % 32) and k-slice (l / 32).
+// Mapping of a fragment to memory (shared by A = query heads and B = keys, so
+// the contraction pairs equal d):  step ks, lane half hf ->
+//   elements [hf*D/2 + ks*FRAG_ELEMS, +FRAG_ELEMS) of the D-vector.
+// Each lane therefore reads one contiguous D/2-element half of a row.
+// ---------------------------------------------------------------------------
+template <int DT>
+struct Fmt;
+
+template <>
+struct Fmt<kBF16> {
+  static constexpr int ESZ = 2;          // bytes per element
+  static constexpr int KSTEP = 16;       // contraction depth of one instruction
+  static constexpr int FRAG_ELEMS = 8;   // elements per lane per instruction
+  static constexpr int FRAG_BYTES = 16;
+  using frag = i32x4;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Fmt<kFP8> {
+  static constexpr int ESZ = 1;
+  static constexpr int KSTEP = 64;
+  static constexpr int FRAG_ELEMS = 32;
+  static constexpr int FRAG_BYTES = 32;
+  using frag = i32x8;
+  // OCP E4M3 operands (format selector 0 for A and B), unit block scales
+  // (E8M0 exponent 127 = 2^0).
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+template <int DT>
+__device__ inline typename Fmt<DT>::frag load_frag(const uint8_t* p) {
+  if constexpr (DT == kBF16) {
+    return *reinterpret_cast<const i32x4*>(p);
+  } else {
+    i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+    i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+template <int DT>
+__device__ inline typename Fmt<DT>::frag zero_frag() {
+  return typename Fmt<DT>::frag{};
+}
+
+// Byte offset, inside one D-row, of the fragment of step ks for lane half hf.
+template <int DT, int D>
+__device__ constexpr int frag_offset(int ks, int hf) {
+  return (hf * (D / 2) + ks * Fmt<DT>::FRAG_ELEMS) * Fmt<DT>::ESZ;
+}
+
+// Row (M index inside a 32-row block) held by accumulator i of lane l in a
+// 32x32 tile: blocks of 4 rows, alternating between the two lane halves.
+__device__ constexpr int acc_row(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving 32-bit key of a float score (larger score -> larger key);
+// -0 is folded onto +0 so equal scores get equal keys.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// Storage codecs used by the proxy step.
+// ---------------------------------------------------------------------------
+__device__ inline float bf16_to_f32(uint16_t c) { return __uint_as_float((uint32_t)c << 16); }
+
+// binary32 -> bf16 with round-to-nearest-even: add 0x7FFF plus the lowest
+// kept bit, then truncate.
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// OCP E4M3FN code -> float (exact).
+__device__ inline float e4m3_to_f32(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  float mag = (e == 0) ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+  if (e == 15 && m == 7) mag = __uint_as_float(0x7FC00000u);
+  return (c & 0x80) ? -mag : mag;
+}
+
+// binary32 -> E4M3FN, round to nearest even, saturating to +-448.  The value is
+// scaled by a power of two so that the 3 kept mantissa bits become the integer
+// part, rounded with rintf (ties to even), and re-assembled.
+__device__ inline uint8_t f32_to_e4m3_rne_sat(float x) {
+  if (x != x) return 0x7F;
+  const uint8_t sign = (__float_as_uint(x) >> 31) ? 0x80 : 0x00;
+  const float a = fabsf(x);
+  if (a >= 448.0f) return sign | 0x7E;
+  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9
+    const int m = (int)rintf(ldexpf(a, 9));  // 0..8; 8 is the smallest normal (code 0x08)
+    return sign | (uint8_t)m;
+  }
+  int E = ilogbf(a);  // a = 1.f * 2^E, E in [-6, 8]
+  int m = (int)rintf(ldexpf(a, 3 - E));  // in [8, 16]
+  if (m == 16) {
+    m = 8;
+    ++E;
+  }
+  int code = ((E + 7) << 3) | (m - 8);
+  if (code > 0x7E) code = 0x7E;
+  return sign | (uint8_t)code;
+}
+
+// ---------------------------------------------------------------------------
+// Wave / block scans.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t wave_inclusive_sum(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Block-wide exclusive sum over NT threads; `scratch` holds NT/64 + 1 words.
+// Returns the exclusive prefix; *total receives the block total.
+template <int NT>
+__device__ inline uint32_t block_exclusive_sum(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t inc = wave_inclusive_sum(v);
+  if (lane == 63) scratch[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t t = lane < NW ? scratch[lane] : 0u;
+    uint32_t ti = wave_inclusive_sum(t);
+    if (lane < NW) scratch[lane] = ti - t;
+    if (lane == NW - 1) scratch[NW] = ti;
+  }
+  __syncthreads();
+  uint32_t res = scratch[wid] + inc - v;
+  *total = scratch[NW];
+  __syncthreads();
+  return res;
+}
+
+}  // namespace pivot

@@ -1,0 +1,124 @@
+// pivot_kernels.h -- argument blocks and launch wrappers of the PIVOT kernels
+// (internal to libpivot; the public ABI is include/pivot.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pivot {
+
+// Proxy mean over groups of g consecutive rows of q[R][H][D].
+struct ProxyArgs {
+  const uint8_t* q;
+  const float* q_scale;
+  const float* w;
+  int R, H, D, g;
+  uint8_t* qbar;
+  float* qbar_scale;
+  float* wbar;
+};
+
+// Causal scan of query rows [row_begin, row_end) against keys k[0..Lk).
+// Row r sees keys 0..pos(r), pos(r) = min(r*pos_mul + pos_add, pos_cap), and
+// writes its scores to S + (r - row_begin)*ldS.
+struct ScanArgs {
+  const uint8_t* q;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k;
+  const float* k_scale;
+  int Lk, H;
+  int row_begin, row_end;
+  int pos_mul, pos_add, pos_cap;
+  int kc;  // keys per workgroup (multiple of 32)
+  float* S;
+  long long ldS;
+};
+
+// Members of groups [grp_begin, grp_end) score their group's candidates.
+// kind 0 (prefill): group j = rows [j*g, min(L, j*g+g)), keys k[0..L).
+// kind 1 (decode):  group j = rows [j*g, j*g+g) of sequence j, keys
+//                   k[j*Lmax ...], cache_len[j] keys.
+// Candidates of group j: cand + (j - grp_begin)*ldc, m slots, ascending, -1 tail.
+// Member row r writes slot scores to S + (r - row_base)*ldS.
+struct RefineArgs {
+  const uint8_t* q;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k;
+  const float* k_scale;
+  int H, kind, L, g, Lmax;
+  const int32_t* cache_len;
+  int grp_begin, grp_end;
+  const int32_t* cand;
+  int ldc, m;
+  int slot_chunk;
+  float* S;
+  long long ldS;
+  int row_base;
+};
+
+// Decode scan: for each sequence b, qr query rows (rows b*qr .. b*qr+qr-1 of
+// q) scan the sequence's cache_len[b] keys.  qr == 1: the proxy, which sees
+// every key; otherwise the g members, member i seeing keys 0..n_b-g+i.
+struct DecScanArgs {
+  const uint8_t* q;
+  const float* q_scale;
+  const float* w;
+  const uint8_t* k;
+  const float* k_scale;
+  int Lmax, H;
+  const int32_t* cache_len;
+  int g, qr;
+  int kc;
+  float* S;
+  long long ldS;
+};
+
+// Row-length rules of the top-m selection.
+enum : int {
+  kLenPos = 0,         // n = pos(R) + 1, positions = slots
+  kLenCache = 1,       // decode proxy row b: n = cache_len[b]
+  kLenDecodeDense = 2, // decode member row b*g+i: n = cache_len[b] - g + i + 1
+  kLenRefine = 3,      // member row: n = #candidates <= its position, positions = cand[slot]
+};
+
+struct TopkArgs {
+  const float* S;
+  long long ldS;
+  int row_begin, nrows;
+  int m;
+  int32_t* out;
+  long long ldo;
+  int kind;
+  int pos_mul, pos_add, pos_cap;  // kLenPos
+  int decode;                     // kLenRefine: 0 prefill, 1 decode
+  int g, Lmax;
+  const int32_t* cache_len;
+  const int32_t* map;  // kLenRefine: candidate lists
+  int ldmap, map_grp_begin;
+};
+
+// Reuse: member rows [row_begin, row_end) receive their group's proxy top-k
+// clipped to their own prefix.
+struct BroadcastArgs {
+  const int32_t* ptop;
+  int ldp, grp_begin;
+  int32_t* out;
+  int topk;
+  int decode, g, Lmax;
+  const int32_t* cache_len;
+  int row_begin, row_end;
+};
+
+hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st);
+hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st);
+hipError_t launch_refine(const RefineArgs& a, int dtype, int D, hipStream_t st);
+hipError_t launch_decode_scan(const DecScanArgs& a, int dtype, int D, int B, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+hipError_t launch_broadcast(const BroadcastArgs& a, hipStream_t st);
+hipError_t launch_selftest_mfma(int32_t* out, hipStream_t st);
+
+bool score_shape_supported(int dtype, int D);
+
+}  // namespace pivot
