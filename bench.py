@@ -49,6 +49,8 @@ def parse():
                     help="time only the headline step (used under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the CPU-oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run 3 plain 1 GiB device copies (counter calibration)")
     return ap.parse_args()
 
 
@@ -128,6 +130,15 @@ def main():
     import top_token_selection_pivot_amd as pv
 
     pv.load()
+    if args.calibrate_copy:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per dispatch
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
     L, H, D, g, topk, C = 131072, 64, 128, args.g, 2048, 4096
     log("generating the 128K prefill inputs")
     inp = synth.make("prefill_128k")
@@ -249,8 +260,8 @@ def main():
         dec = synth.make("decode_mtp_b32")
         dd = upload(dec, torch)
         B, Lmax = dec.B, dec.Lmax
-        dws = torch.empty(pv.decode_workspace_size(B, Lmax, H, D, 2, topk, C, "refine", 1),
-                          dtype=torch.uint8, device="cuda")
+        dws = torch.empty(max(pv.decode_workspace_size(B, Lmax, H, D, 2, topk, C, m, 1)
+                              for m in ("refine", "dense")), dtype=torch.uint8, device="cuda")
         dout = torch.empty((B, 2, topk), dtype=torch.int32, device="cuda")
 
         def dstep(mode="refine"):

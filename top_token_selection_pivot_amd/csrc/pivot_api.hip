@@ -87,13 +87,13 @@ size_t prefill_bytes(const PrefillPlan& p, int rows, bool dense) {
 }
 
 int chunk_rows_for(const PrefillPlan& p, size_t ws, bool dense) {
-  // largest multiple of 8 rows (or all rows) that fits
+  // all rows, else the largest multiple of 8 rows that fits
   if (prefill_bytes(p, p.G, dense) <= ws) return p.G;
-  if (ws < p.fixed + 3 * kAlign) return 0;
-  long long rows = (long long)((ws - p.fixed - 3 * kAlign) / p.per_chunk_row);
-  rows = rows / 8 * 8;
+  if (ws <= p.fixed) return 0;
+  long long rows = (long long)((ws - p.fixed) / p.per_chunk_row) / 8 * 8 + 8;
+  rows = std::min<long long>(rows, (long long)p.G / 8 * 8);
   while (rows > 0 && prefill_bytes(p, (int)rows, dense) > ws) rows -= 8;
-  return (int)std::min<long long>(rows, p.G);
+  return (int)rows;
 }
 
 int validate_common(const void* q, const float* q_scale, const float* w, const void* k,
