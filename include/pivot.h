@@ -39,7 +39,8 @@
  *    max 448) with one float32 scale per token, which must be > 0.  NaN or Inf
  *    inputs are outside the contract.
  *  - Supported shapes: 1 <= H <= 64; D in {32, 64, 128, 256} for bf16 and
- *    {64, 128, 256} for fp8.  q and k 16-byte aligned, w / scales / out
+ *    {64, 128, 256} for fp8; one sequence's keys (L*D or Lmax*D codes) below
+ *    2 GiB.  q and k 16-byte aligned, w / scales / out
  *    4-byte aligned.
  *  - Output rows list positions in ascending order; a row holding fewer than
  *    topk positions is padded with -1 at its tail.  Among equal scores the

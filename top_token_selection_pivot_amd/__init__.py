@@ -33,7 +33,8 @@ BF16, FP8 = 0, 1
 _MODES = {"dense": DENSE, "reuse": REUSE, "refine": REFINE}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpivot.so")
+# the in-tree build; PIVOT_LIBRARY may name another build of the same ABI
+_LIB_PATH = os.environ.get("PIVOT_LIBRARY") or os.path.join(_HERE, "libpivot.so")
 _lib = None
 
 

@@ -189,6 +189,8 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
   if (st) return st;
   if (L < 1) return fail(PIVOT_ERR_SHAPE, "L=%d must be >= 1", L);
   if ((long long)L * H * D > (1ll << 40)) return fail(PIVOT_ERR_SHAPE, "L*H*D too large");
+  if ((long long)L * D * esize(dtype) >= (1ll << 31))
+    return fail(PIVOT_ERR_SHAPE, "the key array (L*D codes) must stay below 2 GiB");
   if (!out && !cand_user) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
   if ((out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)))
     return fail(PIVOT_ERR_ALIGN, "output must be 4-byte aligned");
@@ -397,6 +399,8 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   if (B < 1 || Lmax < 1) return fail(PIVOT_ERR_SHAPE, "B=%d and Lmax=%d must be >= 1", B, Lmax);
   if (g > Lmax) return fail(PIVOT_ERR_PARAM, "g=%d exceeds Lmax=%d", g, Lmax);
   if ((long long)B * Lmax * D > (1ll << 40)) return fail(PIVOT_ERR_SHAPE, "B*Lmax*D too large");
+  if ((long long)Lmax * D * esize(dtype) >= (1ll << 31))
+    return fail(PIVOT_ERR_SHAPE, "one sequence's key cache (Lmax*D codes) must stay below 2 GiB");
   if (!cache_len || (!out && !cand_user) || !workspace)
     return fail(PIVOT_ERR_NULL, "cache_len, out and workspace must be non-NULL");
   if (!aligned(cache_len, 4) || (out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)))

@@ -9,11 +9,12 @@
 // fused with the ReLU, the head weights and the head sum; only the final
 // per-(row, key) score is written.
 //
-// Three kernels:
-//  * scan_kernel:        8 query rows per workgroup (one wave each) share
-//                        32-key tiles staged in LDS; causal: row r stops at pos(r).
-//  * refine_kernel:      the members of one group score the group's candidate
-//                        keys, gathered from the key cache into LDS.
+// Two kernels:
+//  * score_block_kernel: 8 query rows per workgroup (one wave each) share key
+//                        tiles staged in LDS.  Full-prefix scan: contiguous
+//                        keys, row r keeps keys <= pos(r).  Refine: the members
+//                        of one group score the group's candidate keys,
+//                        gathered from the key cache through its candidate list.
 //  * decode_scan_kernel: one sequence's 1-2 query rows stream that sequence's
 //                        key cache straight into registers (no reuse to stage).
 #pragma once
@@ -21,10 +22,13 @@
 #include "pivot_device.h"
 #include "pivot_kernels.h"
 
+#ifndef PIVOT_SCAN_SCHED
+#define PIVOT_SCAN_SCHED 1
+#endif
+
 namespace pivot {
 
-constexpr int kScanRows = 8;      // query rows (waves) per scan workgroup
-constexpr int kScanThreads = kScanRows * kWave;
+constexpr int kScanRows = 8;      // query rows (waves) per scoring workgroup
 constexpr int kLdsPad = 16;       // bytes of padding per staged key row
 
 // Per-wave query state: A fragments of every head block and contraction step,
@@ -54,34 +58,70 @@ struct QueryRegs {
   }
 };
 
-// Contract one 32-key tile whose B fragments are produced by `bfrag(ks)`, then
-// apply ReLU, head weights and the head sum.  Returns, in lanes 0..31, the
-// score of key (tile + lane) (lanes 32..63 hold the same values).
+template <int HB>
+struct TileAcc {
+  f32x16 v[HB];
+};
+
+// Contract one 32-key tile whose B fragments are produced by `bfrag(ks)`:
+// acc.v[mb][i] = q[head(mb, i, lane)] . k[tile + lane % 32].
 template <int DT, int D, int HB, typename BF>
-__device__ inline float score_tile(const QueryRegs<DT, D, HB>& qr, BF bfrag) {
+__device__ inline void mma_tile(const QueryRegs<DT, D, HB>& qr, BF bfrag, TileAcc<HB>& acc) {
   constexpr int NKS = D / Fmt<DT>::KSTEP;
-  f32x16 acc[HB];
 #pragma unroll
-  for (int mb = 0; mb < HB; ++mb) acc[mb] = f32x16{};
+  for (int mb = 0; mb < HB; ++mb) acc.v[mb] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const typename Fmt<DT>::frag b = bfrag(ks);
 #pragma unroll
-    for (int mb = 0; mb < HB; ++mb) acc[mb] = Fmt<DT>::mma(qr.a[mb][ks], b, acc[mb]);
+    for (int mb = 0; mb < HB; ++mb) acc.v[mb] = Fmt<DT>::mma(qr.a[mb][ks], b, acc.v[mb]);
   }
+}
+
+// max(0, x) on the bits of a finite float: every negative float (and -0) has
+// a negative signed-integer pattern, so an integer max with 0 gives +0 there
+// and leaves non-negative values unchanged.  One integer op, which (unlike a
+// float max) needs no NaN-quieting of the matrix-core result first.
+__device__ inline float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Per-lane part of ReLU, head weights and head sum of one contracted tile:
+// the sum over the 16*HB heads this lane holds for its key column.
+template <int DT, int D, int HB>
+__device__ inline float tile_partial(const QueryRegs<DT, D, HB>& qr, const TileAcc<HB>& acc) {
   float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
   for (int mb = 0; mb < HB; ++mb) {
 #pragma unroll
     for (int i = 0; i < 16; i += 4) {
-      p0 = fmaf(qr.wv[mb][i + 0], fmaxf(acc[mb][i + 0], 0.f), p0);
-      p1 = fmaf(qr.wv[mb][i + 1], fmaxf(acc[mb][i + 1], 0.f), p1);
-      p2 = fmaf(qr.wv[mb][i + 2], fmaxf(acc[mb][i + 2], 0.f), p2);
-      p3 = fmaf(qr.wv[mb][i + 3], fmaxf(acc[mb][i + 3], 0.f), p3);
+      p0 = fmaf(qr.wv[mb][i + 0], relu(acc.v[mb][i + 0]), p0);
+      p1 = fmaf(qr.wv[mb][i + 1], relu(acc.v[mb][i + 1]), p1);
+      p2 = fmaf(qr.wv[mb][i + 2], relu(acc.v[mb][i + 2]), p2);
+      p3 = fmaf(qr.wv[mb][i + 3], relu(acc.v[mb][i + 3]), p3);
     }
   }
-  float part = (p0 + p1) + (p2 + p3);
-  return part + __shfl_xor(part, 32, 64);
+  return (p0 + p1) + (p2 + p3);
+}
+
+// Finish two tiles at once: the two lane halves hold the other half of the
+// heads, so one lane-half swap (rows of 32 lanes) plus one add leaves tile A's
+// 32 scores in lanes 0..31 and tile B's in lanes 32..63.
+__device__ inline float pair_combine(float pa, float pb) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One tile: every lane ends with the score of key (tile + lane % 32).
+template <int DT, int D, int HB>
+__device__ inline float tile_epilogue(const QueryRegs<DT, D, HB>& qr, const TileAcc<HB>& acc) {
+  const float p = tile_partial<DT, D, HB>(qr, acc);
+  return pair_combine(p, p);
+}
+
+template <int DT, int D, int HB, typename BF>
+__device__ inline float score_tile(const QueryRegs<DT, D, HB>& qr, BF bfrag) {
+  TileAcc<HB> acc;
+  mma_tile<DT, D, HB>(qr, bfrag, acc);
+  return tile_epilogue<DT, D, HB>(qr, acc);
 }
 
 // Staged key tile in LDS: kTileN rows of D codes, padded.
@@ -95,150 +135,233 @@ struct KeyTile {
 
 // ---------------------------------------------------------------------------
 // Prefill full-prefix scan.
+//
+// A workgroup = 8 waves = 8 consecutive query rows, over a chunk of kc keys.
+// Keys are staged in LDS in stages of kStageTiles tiles of 32 keys (double
+// buffered: the next stage is loaded into registers during the current one
+// and stored to LDS at its end, one barrier per stage).  Within a stage each
+// wave runs a fixed software pipeline over the tiles, with the B fragments of
+// tile t+1 read from LDS while tile t is contracted, and the epilogue of tile
+// t-1 interleaved with the contraction of tile t:
+//   tile 0: contract; finish and store the previous stage's pair (2,3)
+//   tile 1: contract; partial of tile 0
+//   tile 2: contract; partial of tile 1, store pair (0,1)
+//   tile 3: contract; partial of tile 2
+// Every tile of a stage is contracted; stores beyond a row's causal limit
+// (or the chunk end) fall outside the row's buffer range and are dropped by
+// the hardware range check, so the stage body has no data-dependent branch.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int HB>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
-  using KT = KeyTile<DT, D>;
-  constexpr int NPT = (KT::CHUNKS + kScanThreads - 1) / kScanThreads;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[KT::BYTES];
+constexpr int kStageTiles = 4;
+constexpr uint32_t kBufferFlags = 0x00020000;  // raw 32-bit buffer, range-checked
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int rb = a.row_begin + blockIdx.y * kScanRows;
-  const int rlast = min(rb + kScanRows, a.row_end) - 1;
-  const int lim = min(rlast * a.pos_mul + a.pos_add, a.pos_cap) + 1;  // keys 0..lim-1
-  const int k0 = blockIdx.x * a.kc;
-  if (k0 >= lim) return;
-  const int k1 = min(k0 + a.kc, lim);
-
-  const int r = rb + wid;
-  const bool active = r <= rlast;
-  const int pos = active ? min(r * a.pos_mul + a.pos_add, a.pos_cap) : -1;
-
-  QueryRegs<DT, D, HB> qr;
-  float qs = 1.f;
-  if (active) {
-    qr.load(a.q + (size_t)r * a.H * D * Fmt<DT>::ESZ, a.w + (size_t)r * a.H, a.H, lane);
-    if constexpr (DT == kFP8) qs = a.q_scale[r];
-  }
-
-  i32x4 pre[NPT];
-  auto fetch = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int c = tid + i * kScanThreads;
-      pre[i] = i32x4{};
-      if (c < KT::CHUNKS) {
-        const int key = t0 + c / (KT::ROW / 16);
-        if (key < a.Lk)
-          pre[i] = *reinterpret_cast<const i32x4*>(a.k + (size_t)key * KT::ROW +
-                                                   (c % (KT::ROW / 16)) * 16);
-      }
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int c = tid + i * kScanThreads;
-      if (c < KT::CHUNKS)
-        *reinterpret_cast<i32x4*>(tile + (c / (KT::ROW / 16)) * KT::STRIDE +
-                                  (c % (KT::ROW / 16)) * 16) = pre[i];
-    }
-  };
-
-  float* srow = a.S + (long long)(r - a.row_begin) * a.ldS;
-  const int hf = lane >> 5, n = lane & 31;
-  fetch(k0);
-  for (int t0 = k0; t0 < k1; t0 += kTileN) {
-    __syncthreads();
-    stash();
-    __syncthreads();
-    if (t0 + kTileN < k1) fetch(t0 + kTileN);
-    if (active && t0 <= pos) {
-      const uint8_t* brow = tile + n * KT::STRIDE;
-      float s = score_tile<DT, D, HB>(qr, [&](int ks) {
-        return load_frag<DT>(brow + frag_offset<DT, D>(ks, hf));
-      });
-      const int key = t0 + lane;
-      if (lane < kTileN && key <= pos && key < k1) {
-        if constexpr (DT == kFP8) s = (s * qs) * a.k_scale[key];
-        srow[key] = s;
-      }
-    }
-  }
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
 }
 
-// ---------------------------------------------------------------------------
-// Refine: members of one group score the group's candidates.
-// ---------------------------------------------------------------------------
-template <int DT, int D, int HB>
-__global__ __launch_bounds__(kScanThreads) void refine_kernel(RefineArgs a) {
-  using KT = KeyTile<DT, D>;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[KT::BYTES];
-  __shared__ int32_t tpos[kTileN];
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nthreads = blockDim.x;
-  const int j = a.grp_begin + blockIdx.y;
-
-  // group geometry
-  int row0, nmem, ncand;
-  size_t keybase = 0;
-  const float* kscale = a.k_scale;
-  if (a.kind == 0) {
-    row0 = j * a.g;
-    nmem = min(a.g, a.L - row0);
-    ncand = min(a.m, row0 + nmem);  // min(m, e_j + 1)
-  } else {
-    const int nb = a.cache_len[j];
-    if (nb < a.g || nb > a.Lmax) return;
-    row0 = j * a.g;
-    nmem = a.g;
-    ncand = min(a.m, nb);
-    keybase = (size_t)j * a.Lmax;
-    if constexpr (DT == kFP8) kscale += keybase;
+// Interleaving hint for one tile step: the DS reads of the next tile, the 16
+// contractions and the previous tile's epilogue alternate.
+__device__ inline void sched_tile_step() {
+#if PIVOT_SCAN_SCHED
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
   }
-  const int s0 = blockIdx.x * a.slot_chunk;
-  if (s0 >= ncand) return;
-  const int s1 = min(s0 + a.slot_chunk, ncand);
-  const int mem = blockIdx.z * kScanRows + wid;
-  const bool active = mem < nmem;
-  const int r = row0 + mem;
-  const int32_t* cand = a.cand + (size_t)(j - a.grp_begin) * a.ldc;
-  const uint8_t* kb = a.k + keybase * KT::ROW;
+#endif
+}
+
+constexpr int kScanWaveThreads = kScanRows * kWave;
+
+// Geometry of one workgroup of the scoring loop: its query rows, the key
+// positions it covers and where scores go.
+//  * full-prefix scan (GATHER = false, ScanArgs): rows rb..rb+7, a chunk of
+//    contiguous keys [k0, k1); row r keeps keys <= pos(r).
+//  * Refine (GATHER = true, RefineArgs): the members of one group, a chunk of
+//    candidate slots [k0, k1) whose keys are gathered through the group's
+//    candidate list; every slot < the group's candidate count is kept.
+template <int DT, int D, int HB, bool GATHER, typename Args>
+__global__ __launch_bounds__(kScanWaveThreads) void score_block_kernel(Args a) {
+  using KT = KeyTile<DT, D>;
+  using Frag = typename Fmt<DT>::frag;
+  constexpr int NT = kScanWaveThreads;
+  constexpr int NKS = D / Fmt<DT>::KSTEP;
+  constexpr int SCH = kStageTiles * KT::CHUNKS;  // 16-byte pieces per stage
+  constexpr int NPT = (SCH + NT - 1) / NT;
+  constexpr int STAGE_BYTES = kStageTiles * KT::BYTES;
+  constexpr int STAGE_KEYS = kStageTiles * kTileN;
+  constexpr int RCH = KT::ROW / 16;  // 16-byte pieces per key row
+  static_assert(kStageTiles == 4, "the pipeline below is written for 4 tiles per stage");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- workgroup geometry ----
+  int k0, k1;                 // key positions (scan) or candidate slots (Refine)
+  int r;                      // this wave's query row
+  bool active;                // the row exists
+  int nvalid;                 // scores [0, nvalid) of the row are stored
+  long long srow_index;       // row of S
+  __amdgpu_buffer_rsrc_t krs; // keys: the chunk (scan) or the whole key array (Refine)
+  __amdgpu_buffer_rsrc_t crs; // Refine: candidate positions of slots [k0, k1)
+  __amdgpu_buffer_rsrc_t ksr; // fp8 key scales (empty for bf16)
+  if constexpr (!GATHER) {
+    const int rb = a.row_begin + blockIdx.y * kScanRows;
+    const int rlast = min(rb + kScanRows, a.row_end) - 1;
+    const int lim = min(rlast * a.pos_mul + a.pos_add, a.pos_cap) + 1;  // keys 0..lim-1
+    k0 = blockIdx.x * a.kc;
+    if (k0 >= lim) return;
+    k1 = min(k0 + a.kc, lim);
+    r = rb + wid;
+    active = r <= rlast;
+    const int pos = active ? min(r * a.pos_mul + a.pos_add, a.pos_cap) : -1;
+    nvalid = active ? min(pos + 1, k1) : 0;
+    srow_index = active ? r - a.row_begin : 0;
+    krs = make_rsrc(a.k + (size_t)k0 * KT::ROW, (uint32_t)(k1 - k0) * KT::ROW);
+    crs = krs;
+    ksr = make_rsrc(DT == kFP8 ? a.k_scale + k0 : a.S, DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u);
+  } else {
+    const int j = a.grp_begin + blockIdx.y;
+    int row0, nmem, ncand, nkeys;
+    size_t keybase = 0;
+    if (a.kind == 0) {
+      row0 = j * a.g;
+      nmem = min(a.g, a.L - row0);
+      ncand = min(a.m, row0 + nmem);  // min(m, e_j + 1)
+      nkeys = a.L;
+    } else {
+      const int nb = a.cache_len[j];
+      if (nb < a.g || nb > a.Lmax) return;
+      row0 = j * a.g;
+      nmem = a.g;
+      ncand = min(a.m, nb);
+      nkeys = nb;
+      keybase = (size_t)j * a.Lmax;
+    }
+    k0 = blockIdx.x * a.slot_chunk;
+    if (k0 >= ncand) return;
+    k1 = min(k0 + a.slot_chunk, ncand);
+    const int mem = blockIdx.z * kScanRows + wid;
+    active = mem < nmem;
+    r = row0 + (active ? mem : 0);
+    nvalid = active ? k1 : 0;
+    srow_index = r - a.row_base;
+    krs = make_rsrc(a.k + keybase * KT::ROW, (uint32_t)nkeys * KT::ROW);
+    crs = make_rsrc(a.cand + (size_t)(j - a.grp_begin) * a.ldc + k0, (uint32_t)(k1 - k0) * 4u);
+    ksr = make_rsrc(DT == kFP8 ? a.k_scale + keybase : a.q_scale, DT == kFP8 ? (uint32_t)nkeys * 4u : 0u);
+  }
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.S + srow_index * a.ldS, (uint32_t)nvalid * 4u);
 
   QueryRegs<DT, D, HB> qr;
   float qs = 1.f;
   if (active) {
     qr.load(a.q + (size_t)r * a.H * D * Fmt<DT>::ESZ, a.w + (size_t)r * a.H, a.H, lane);
     if constexpr (DT == kFP8) qs = a.q_scale[r];
-  }
-  float* srow = a.S + (long long)(r - a.row_base) * a.ldS;
-  const int hf = lane >> 5, n = lane & 31;
-
-  for (int t0 = s0; t0 < s1; t0 += kTileN) {
-    __syncthreads();
-    if (tid < kTileN) tpos[tid] = (t0 + tid < s1) ? cand[t0 + tid] : -1;
-    __syncthreads();
-    for (int c = tid; c < KT::CHUNKS; c += nthreads) {
-      const int kr = c / (KT::ROW / 16), part = c % (KT::ROW / 16);
-      const int p = tpos[kr];
-      i32x4 v = i32x4{};
-      if (p >= 0) v = *reinterpret_cast<const i32x4*>(kb + (size_t)p * KT::ROW + part * 16);
-      *reinterpret_cast<i32x4*>(tile + kr * KT::STRIDE + part * 16) = v;
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < HB; ++mb) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qr.a[mb][ks] = zero_frag<DT>();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qr.wv[mb][i] = 0.f;
     }
-    __syncthreads();
-    if (active) {
-      const uint8_t* brow = tile + n * KT::STRIDE;
-      float s = score_tile<DT, D, HB>(qr, [&](int ks) {
-        return load_frag<DT>(brow + frag_offset<DT, D>(ks, hf));
-      });
-      const int slot = t0 + lane;
-      if (lane < kTileN && slot < s1) {
-        if constexpr (DT == kFP8) s = (s * qs) * kscale[tpos[lane]];
-        srow[slot] = s;
+  }
+
+  // key position of slot `slot` (Refine) -- 0 past the candidate list
+  auto cand_pos = [&](int slot) -> int {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(crs, (slot - k0) * 4, 0, 0);
+  };
+
+  i32x4 pre[NPT];
+  auto fetch = [&](int base) {  // stage starting at key/slot `base` -> registers
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + i * NT;
+      if (SCH % NT == 0 || c < SCH) {
+        int off;
+        if constexpr (!GATHER)
+          off = (base - k0) * KT::ROW + c * 16;
+        else
+          off = cand_pos(base + c / RCH) * KT::ROW + (c % RCH) * 16;
+        pre[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
       }
     }
+  };
+  auto stash = [&](int buf) {
+    uint8_t* st = lds + buf * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = tid + i * NT;
+      if (SCH % NT == 0 || c < SCH)
+        *reinterpret_cast<i32x4*>(st + (c / RCH) * KT::STRIDE + (c % RCH) * 16) = pre[i];
+    }
+  };
+
+  const int hf = lane >> 5, n = lane & 31;
+  auto load_b = [&](const uint8_t* st, int tt, Frag* b) {
+    const uint8_t* brow = st + (tt * kTileN + n) * KT::STRIDE;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) b[ks] = load_frag<DT>(brow + frag_offset<DT, D>(ks, hf));
+  };
+  auto contract = [&](const Frag* b, TileAcc<HB>& acc) {
+    mma_tile<DT, D, HB>(qr, [&](int ks) { return b[ks]; }, acc);
+  };
+  // pair of tiles starting at key/slot t0: lane l holds t0 + l
+  auto store_pair = [&](float pa, float pb, int t0) {
+    float s = pair_combine(pa, pb);
+    const int key = t0 + lane;
+    if constexpr (DT == kFP8) {
+      const int kp = GATHER ? cand_pos(key) : key - k0;
+      s = (s * qs) * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksr, kp * 4, 0, 0));
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), srs, key * 4, 0, 0);
+  };
+
+  fetch(k0);
+  stash(0);
+  __syncthreads();
+  if (k0 + STAGE_KEYS < k1) fetch(k0 + STAGE_KEYS);
+
+  TileAcc<HB> acc[2];
+  Frag b0[NKS], b1[NKS];
+  float pa = 0.f;
+  int buf = 0;
+  for (int sb = k0; sb < k1; sb += STAGE_KEYS) {
+    const uint8_t* st = lds + buf * STAGE_BYTES;
+    load_b(st, 0, b0);
+    // tile 0
+    load_b(st, 1, b1);
+    contract(b0, acc[0]);
+    if (sb != k0) store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), sb - STAGE_KEYS + 2 * kTileN);
+    sched_tile_step();
+    // tile 1
+    load_b(st, 2, b0);
+    contract(b1, acc[1]);
+    pa = tile_partial<DT, D, HB>(qr, acc[0]);
+    sched_tile_step();
+    // tile 2
+    load_b(st, 3, b1);
+    contract(b0, acc[0]);
+    store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), sb);
+    sched_tile_step();
+    // tile 3
+    contract(b1, acc[1]);
+    pa = tile_partial<DT, D, HB>(qr, acc[0]);
+    sched_tile_step();
+
+    if (sb + STAGE_KEYS < k1) {
+      stash(buf ^ 1);
+      if (sb + 2 * STAGE_KEYS < k1) fetch(sb + 2 * STAGE_KEYS);
+    }
+    __syncthreads();
+    buf ^= 1;
   }
+  // the last stage's pair (2,3)
+  const int last = k0 + ((k1 - k0 - 1) / STAGE_KEYS) * STAGE_KEYS;
+  store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), last + 2 * kTileN);
 }
 
 // ---------------------------------------------------------------------------

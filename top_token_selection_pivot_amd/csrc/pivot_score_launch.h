@@ -8,11 +8,11 @@ namespace pivot {
 
 template <int DT, int D, int HB>
 static void scan_one(const ScanArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((scan_kernel<DT, D, HB>), grid, dim3(kScanThreads), 0, st, a);
+  hipLaunchKernelGGL((score_block_kernel<DT, D, HB, false, ScanArgs>), grid, dim3(kScanWaveThreads), 0, st, a);
 }
 template <int DT, int D, int HB>
 static void refine_one(const RefineArgs& a, dim3 grid, dim3 block, hipStream_t st) {
-  hipLaunchKernelGGL((refine_kernel<DT, D, HB>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((score_block_kernel<DT, D, HB, true, RefineArgs>), grid, dim3(kScanWaveThreads), 0, st, a);
 }
 template <int DT, int D, int HB>
 static void decode_one(const DecScanArgs& a, dim3 grid, hipStream_t st) {
@@ -57,9 +57,8 @@ hipError_t launch_scan_dt(const ScanArgs& a, int D, hipStream_t st) {
 template <int DT>
 hipError_t launch_refine_dt(const RefineArgs& a, int D, hipStream_t st) {
   const int ngrp = a.grp_end - a.grp_begin;
-  const int waves = a.g < kScanRows ? a.g : kScanRows;
   dim3 grid((a.m + a.slot_chunk - 1) / a.slot_chunk, ngrp, (a.g + kScanRows - 1) / kScanRows);
-  dim3 block(waves * kWave);
+  dim3 block(kScanWaveThreads);
   auto f = [&]<int D_, int HB_>() { refine_one<DT, D_, HB_>(a, grid, block, st); };
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
   return hipGetLastError();
