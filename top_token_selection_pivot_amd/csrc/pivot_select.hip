@@ -35,21 +35,30 @@ bool score_shape_supported(int dtype, int D) {
 // multiply-add, then one correctly rounded division by the member count.
 // ---------------------------------------------------------------------------
 constexpr int kProxyThreads = 256;
+constexpr int kProxyChunk = 16;                                  // elements per 16-element chunk
+constexpr int kProxyMaxCPT = 64 * 256 / kProxyChunk / kProxyThreads;  // chunks per thread (H*D <= 16384)
 
+// The 16 values of chunk c of row `row` (binary32; fp8 codes times the row scale).
 template <int DT>
-__device__ inline float member_value(const ProxyArgs& a, int row, size_t e) {
+__device__ inline void chunk_values(const ProxyArgs& a, int row, int c, float* x) {
+  const size_t HD = (size_t)a.H * a.D;
   if constexpr (DT == kBF16) {
-    return bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[(size_t)row * a.H * a.D + e]);
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(a.q) + (size_t)row * HD + (size_t)c * kProxyChunk;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e + 0] = __uint_as_float((uint32_t)lo[e] << 16);
+      x[2 * e + 1] = __uint_as_float((uint32_t)lo[e] & 0xFFFF0000u);
+      x[8 + 2 * e + 0] = __uint_as_float((uint32_t)hi[e] << 16);
+      x[8 + 2 * e + 1] = __uint_as_float((uint32_t)hi[e] & 0xFFFF0000u);
+    }
   } else {
-    return __fmul_rn(a.q_scale[row], e4m3_to_f32(a.q[(size_t)row * a.H * a.D + e]));
+    const i32x4 v = *reinterpret_cast<const i32x4*>(a.q + (size_t)row * HD + (size_t)c * kProxyChunk);
+    const float s = a.q_scale[row];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = __fmul_rn(s, e4m3_to_f32((uint8_t)((uint32_t)v[e >> 2] >> (8 * (e & 3)))));
   }
-}
-
-template <int DT>
-__device__ inline float group_mean(const ProxyArgs& a, int r0, int n, size_t e) {
-  float s = 0.f;
-  for (int t = 0; t < n; ++t) s = __fadd_rn(s, member_value<DT>(a, r0 + t, e));
-  return __fdiv_rn(s, (float)n);
 }
 
 template <int DT>
@@ -58,10 +67,11 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
   const int r0 = j * a.g;
   const int n = min(a.g, a.R - r0);
   const size_t HD = (size_t)a.H * a.D;
+  const int nch = (int)(HD / kProxyChunk);
   if (n == 1) {  // a one-member group is its member
-    const size_t esz = DT == kBF16 ? 2 : 1;
-    for (size_t e = tid; e < HD * esz; e += kProxyThreads)
-      a.qbar[j * HD * esz + e] = a.q[(size_t)r0 * HD * esz + e];
+    const size_t bytes = HD * (DT == kBF16 ? 2 : 1);
+    for (size_t e = (size_t)tid * 16; e < bytes; e += (size_t)kProxyThreads * 16)
+      *reinterpret_cast<i32x4*>(a.qbar + j * bytes + e) = *reinterpret_cast<const i32x4*>(a.q + (size_t)r0 * bytes + e);
     if (tid == 0) a.qbar_scale[j] = DT == kBF16 ? 1.f : a.q_scale[r0];
     for (int h = tid; h < a.H; h += kProxyThreads) a.wbar[(size_t)j * a.H + h] = a.w[(size_t)r0 * a.H + h];
     return;
@@ -71,22 +81,60 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
     for (int t = 0; t < n; ++t) s = __fadd_rn(s, a.w[(size_t)(r0 + t) * a.H + h]);
     a.wbar[(size_t)j * a.H + h] = __fdiv_rn(s, (float)n);
   }
+  // means of this thread's chunks, members added in ascending position
+  float mean[kProxyMaxCPT][kProxyChunk];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kProxyMaxCPT; ++i) {
+    const int c = tid + i * kProxyThreads;
+    if (c >= nch) continue;
+    float acc[kProxyChunk];
+#pragma unroll
+    for (int e = 0; e < kProxyChunk; ++e) acc[e] = 0.f;
+    for (int t = 0; t < n; ++t) {
+      float x[kProxyChunk];
+      chunk_values<DT>(a, r0 + t, c, x);
+#pragma unroll
+      for (int e = 0; e < kProxyChunk; ++e) acc[e] = __fadd_rn(acc[e], x[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < kProxyChunk; ++e) {
+      mean[i][e] = __fdiv_rn(acc[e], (float)n);
+      amax = fmaxf(amax, fabsf(mean[i][e]));
+    }
+  }
   if constexpr (DT == kBF16) {
-    uint16_t* out = reinterpret_cast<uint16_t*>(a.qbar) + (size_t)j * HD;
-    for (size_t e = tid; e < HD; e += kProxyThreads) out[e] = f32_to_bf16_rne(group_mean<DT>(a, r0, n, e));
+#pragma unroll
+    for (int i = 0; i < kProxyMaxCPT; ++i) {
+      const int c = tid + i * kProxyThreads;
+      if (c >= nch) continue;
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        w[e] = (uint32_t)f32_to_bf16_rne(mean[i][2 * e]) | ((uint32_t)f32_to_bf16_rne(mean[i][2 * e + 1]) << 16);
+      uint16_t* out = reinterpret_cast<uint16_t*>(a.qbar) + (size_t)j * HD + (size_t)c * kProxyChunk;
+      *reinterpret_cast<i32x4*>(out) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *reinterpret_cast<i32x4*>(out + 8) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    }
     if (tid == 0) a.qbar_scale[j] = 1.f;
   } else {
     __shared__ float red[kProxyThreads / kWave];
-    float amax = 0.f;
-    for (size_t e = tid; e < HD; e += kProxyThreads) amax = fmaxf(amax, fabsf(group_mean<DT>(a, r0, n, e)));
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = red[0];
     for (int i = 1; i < kProxyThreads / kWave; ++i) amax = fmaxf(amax, red[i]);
     const float sp = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
-    for (size_t e = tid; e < HD; e += kProxyThreads)
-      a.qbar[(size_t)j * HD + e] = f32_to_e4m3_rne_sat(__fdiv_rn(group_mean<DT>(a, r0, n, e), sp));
+#pragma unroll
+    for (int i = 0; i < kProxyMaxCPT; ++i) {
+      const int c = tid + i * kProxyThreads;
+      if (c >= nch) continue;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w[e >> 2] |= (uint32_t)f32_to_e4m3_rne_sat(__fdiv_rn(mean[i][e], sp)) << (8 * (e & 3));
+      *reinterpret_cast<i32x4*>(a.qbar + (size_t)j * HD + (size_t)c * kProxyChunk) =
+          i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
     if (tid == 0) a.qbar_scale[j] = sp;
   }
 }
@@ -102,14 +150,26 @@ hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Exact top-m of one score row (tutorial "Sparse Attention의 Indexer",
-// Figure 1: keep the positions of the m largest scores).  Radix select over
-// the order-preserving 32-bit keys, most significant digit first (11, 11 and
-// 10 bits, LDS histograms), finds the m-th largest key T and how many keys
-// equal to T are taken; an index-ordered compaction then emits every key
-// above T and the first such keys equal to T, so equal scores go to the lower
+// Figure 1: keep the positions of the m largest scores).
+//
+// Radix select over order-preserving 32-bit keys, most significant digit
+// first, with LDS histograms.  It finds the m-th largest key T and how many
+// keys equal to T are taken; an index-ordered compaction then emits every key
+// above T and the first keys equal to T, so equal scores go to the lower
 // position and the output is ascending.
+//
+// Pass 1 reads the row once (16-byte loads, four in flight per thread) and
+// histograms its top 12 bits.  Every key at or above the threshold bin is then
+// gathered into LDS in index order (a row that fits is staged whole during
+// pass 1); the remaining 20 bits and the emission run on that LDS copy, so a
+// row is read from memory at most twice.  If the threshold bin is too crowded
+// for LDS (e.g. a huge run of equal scores), the selection falls back to
+// further passes over the row in memory.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
+constexpr int kTopkCap = 7680;     // keys staged in LDS
+constexpr int kTopkBits1 = 12;     // first digit: bits 31..20
+constexpr int kTopkU = 4;          // 16-byte loads in flight per thread
 
 __device__ inline int ref_count(const int32_t* list, int m, int t) {
   // number of leading entries of the ascending, -1 padded list that are in [0, t]
@@ -155,73 +215,68 @@ __device__ inline int row_length(const TopkArgs& a, int R, const int32_t** list)
   }
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t scratch[kTopkThreads / kWave + 1];
-  __shared__ uint32_t sh_digit, sh_rem;
-
+// The bin (of nbins, counted from the top) that holds the rem-th largest key;
+// *above receives the number of keys in higher bins.  Thread t owns the
+// nbins/NT consecutive bins that start nbins-1-t*(nbins/NT) and go down.
+template <int NT>
+__device__ inline void find_bin(const uint32_t* hist, int nbins, uint32_t rem, uint32_t* scratch,
+                                uint32_t* sh_bin, uint32_t* sh_above) {
   const int tid = threadIdx.x;
-  const int i = blockIdx.x;
-  const int R = a.row_begin + i;
-  const float* row = a.S + (long long)i * a.ldS;
-  int32_t* out = a.out + (long long)i * a.ldo;
-  const int32_t* list;
-  const int n = row_length(a, R, &list);
-  const int m = a.m;
-
-  if (n <= m) {
-    for (int s = tid; s < m; s += kTopkThreads) out[s] = s < n ? (list ? list[s] : s) : -1;
-    return;
-  }
-
-  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)m;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const uint32_t nb = 1u << widths[pass];
-    for (uint32_t b = tid; b < nb; b += kTopkThreads) hist[b] = 0;
-    __syncthreads();
-    for (int s = tid; s < n; s += kTopkThreads) {
-      const uint32_t key = score_key(row[s]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+  const int bpt = nbins / NT;  // 1 or 4
+  uint32_t c[4] = {0u, 0u, 0u, 0u}, sum = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (e < bpt) {
+      c[e] = hist[nbins - 1 - tid * bpt - e];
+      sum += c[e];
     }
-    __syncthreads();
-    // thread t owns bins nb-1-2t and nb-2-2t (descending), so an inclusive
-    // scan over threads counts keys from the top bin down
-    const int b0 = (int)nb - 1 - 2 * tid, b1 = b0 - 1;
-    const bool own = 2 * tid < (int)nb;
-    const uint32_t c0 = own ? hist[b0] : 0u, c1 = own ? hist[b1] : 0u;
-    uint32_t tot;
-    const uint32_t excl = block_exclusive_sum<kTopkThreads>(c0 + c1, scratch, &tot);
-    if (own) {
-      if (excl < rem && rem <= excl + c0) {
-        sh_digit = (uint32_t)b0;
-        sh_rem = rem - excl;
-      } else if (excl + c0 < rem && rem <= excl + c0 + c1) {
-        sh_digit = (uint32_t)b1;
-        sh_rem = rem - excl - c0;
+  uint32_t tot;
+  uint32_t run = block_exclusive_sum<NT>(sum, scratch, &tot);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (e < bpt) {
+      if (run < rem && rem <= run + c[e]) {
+        *sh_bin = (uint32_t)(nbins - 1 - tid * bpt - e);
+        *sh_above = run;
       }
+      run += c[e];
     }
-    __syncthreads();
-    prefix |= sh_digit << shift;
-    pmask |= (nb - 1) << shift;
-    rem = sh_rem;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const uint32_t need_eq = rem;           // keys equal to T to take, lowest positions first
-  const uint32_t need_gt = (uint32_t)m - need_eq;
+  __syncthreads();
+}
 
+// Loads the 4 scores at s0..s0+3 of a row of n (s0 a multiple of 4).
+__device__ inline float4 load4(const float* row, int s0, int n) {
+  if (s0 + 3 < n) return *reinterpret_cast<const float4*>(row + s0);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (s0 + 0 < n) v.x = row[s0 + 0];
+  if (s0 + 1 < n) v.y = row[s0 + 1];
+  if (s0 + 2 < n) v.z = row[s0 + 2];
+  return v;
+}
+
+__device__ inline float f4(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+
+// Emits, in index order, the entries of a sequence that are selected by
+// (T, need_eq): keys above T, and the first need_eq keys equal to T.  The
+// sequence is given by get(i) -> (key, slot) for i < cnt; each thread takes
+// 4*kTopkU consecutive entries per round.
+template <typename Get>
+__device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint32_t m, const int32_t* list,
+                                     int32_t* out, uint32_t* scratch, Get get) {
+  constexpr int E = 4 * kTopkU;
+  const int tid = threadIdx.x;
+  const uint32_t need_gt = m - need_eq;
   uint32_t g_gt = 0, g_eq = 0;
-  for (int base = 0; base < n; base += 4 * kTopkThreads) {
-    const int s0 = base + 4 * tid;
-    uint32_t key[4];
+  for (int base = 0; base < cnt; base += E * kTopkThreads) {
+    const int i0 = base + tid * E;
+    uint32_t key[E];
+    int slot[E];
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      key[e] = s0 + e < n ? score_key(row[s0 + e]) : 0u;
-      const bool valid = s0 + e < n;
+    for (int e = 0; e < E; ++e) {
+      const bool valid = i0 + e < cnt;
+      if (valid) get(i0 + e, &key[e], &slot[e]);
+      else { key[e] = 0u; slot[e] = -1; }
       cgt += (valid && key[e] > T) ? 1u : 0u;
       ceq += (valid && key[e] == T) ? 1u : 0u;
     }
@@ -229,16 +284,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const uint32_t excl = block_exclusive_sum<kTopkThreads>(cgt | (ceq << 16), scratch, &tot);
     uint32_t gt_before = g_gt + (excl & 0xFFFFu), eq_before = g_eq + (excl >> 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (s0 + e >= n) break;
-      const int slot = s0 + e;
+    for (int e = 0; e < E; ++e) {
+      if (slot[e] < 0) continue;
       if (key[e] > T) {
-        const uint32_t pos = gt_before + min(eq_before, need_eq);
-        if (pos < (uint32_t)m) out[pos] = list ? list[slot] : slot;
+        const uint32_t p = gt_before + min(eq_before, need_eq);
+        if (p < m) out[p] = list ? list[slot[e]] : slot[e];
         ++gt_before;
       } else if (key[e] == T) {
-        const uint32_t pos = gt_before + eq_before;
-        if (eq_before < need_eq && pos < (uint32_t)m) out[pos] = list ? list[slot] : slot;
+        const uint32_t p = gt_before + eq_before;
+        if (eq_before < need_eq && p < m) out[p] = list ? list[slot[e]] : slot[e];
         ++eq_before;
       }
     }
@@ -248,9 +302,319 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+  constexpr int NT = kTopkThreads;
+  constexpr int NB1 = 1 << kTopkBits1;
+  __shared__ uint32_t hist[NB1];
+  __shared__ uint32_t ckey[kTopkCap];
+  __shared__ int32_t cslot[kTopkCap];
+  __shared__ uint32_t scratch[NT / kWave + 1];
+  __shared__ uint32_t sh_bin, sh_above;
+
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x;
+  const int R = a.row_begin + i;
+  const float* row = a.S + (long long)i * a.ldS;
+  int32_t* out = a.out + (long long)i * a.ldo;
+  const int32_t* list;
+  const int n = row_length(a, R, &list);
+  const uint32_t m = (uint32_t)a.m;
+
+  if (n <= (int)m) {
+    for (int s = tid; s < (int)m; s += NT) out[s] = s < n ? (list ? list[s] : s) : -1;
+    return;
+  }
+
+  // ---- pass 1: histogram of the top 12 bits (rows that fit are staged in LDS)
+  const bool whole = n <= kTopkCap;
+  for (int b = tid; b < NB1; b += NT) hist[b] = 0u;
+  __syncthreads();
+  for (int base = 0; base < n; base += kTopkU * NT * 4) {
+    float4 v[kTopkU];
+#pragma unroll
+    for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
+#pragma unroll
+    for (int u = 0; u < kTopkU; ++u) {
+      const int s0 = base + (u * NT + tid) * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (s0 + e >= n) continue;
+        const uint32_t key = score_key(f4(v[u], e));
+        atomicAdd(&hist[key >> (32 - kTopkBits1)], 1u);
+        if (whole) {
+          ckey[s0 + e] = key;
+          cslot[s0 + e] = s0 + e;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  find_bin<NT>(hist, NB1, m, scratch, &sh_bin, &sh_above);
+  const uint32_t b1 = sh_bin;
+  uint32_t rem = m - sh_above;
+  const uint32_t cand_total = sh_above + hist[b1];
+  __syncthreads();  // hist is cleared below
+
+  int ncand;
+  if (whole) {
+    ncand = n;
+  } else if (cand_total <= (uint32_t)kTopkCap) {
+    // ---- pass 2: gather every key with first digit >= b1 into LDS, in index order
+    constexpr int E = 4 * kTopkU;
+    uint32_t running = 0;
+    for (int base = 0; base < n; base += E * NT) {
+      const int s0 = base + tid * E;
+      float4 v[kTopkU];
+#pragma unroll
+      for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, s0 + 4 * u, n);
+      uint32_t key[E];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        key[e] = score_key(f4(v[e >> 2], e & 3));
+        if (s0 + e < n && (key[e] >> (32 - kTopkBits1)) >= b1) ++cnt;
+      }
+      uint32_t tot;
+      uint32_t p = running + block_exclusive_sum<NT>(cnt, scratch, &tot);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (s0 + e < n && (key[e] >> (32 - kTopkBits1)) >= b1) {
+          ckey[p] = key[e];
+          cslot[p] = s0 + e;
+          ++p;
+        }
+      }
+      running += tot;
+    }
+    ncand = (int)running;
+    __syncthreads();
+  } else {
+    ncand = -1;  // fall back to passes over the row in memory
+  }
+
+  uint32_t prefix = b1 << (32 - kTopkBits1);
+  uint32_t pmask = ~0u << (32 - kTopkBits1);
+  // ---- remaining 20 bits in two 10-bit digits
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    for (int b = tid; b < 1024; b += NT) hist[b] = 0u;
+    __syncthreads();
+    if (ncand >= 0) {
+      for (int c = tid; c < ncand; c += NT) {
+        const uint32_t key = ckey[c];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
+      }
+    } else {
+      for (int base = 0; base < n; base += kTopkU * NT * 4) {
+        float4 v[kTopkU];
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) {
+          const int s0 = base + (u * NT + tid) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (s0 + e >= n) continue;
+            const uint32_t key = score_key(f4(v[u], e));
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    find_bin<NT>(hist, 1024, rem, scratch, &sh_bin, &sh_above);
+    prefix |= sh_bin << shift;
+    pmask |= 1023u << shift;
+    rem -= sh_above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const uint32_t need_eq = rem;  // keys equal to T to take, lowest positions first
+
+  if (ncand >= 0) {
+    emit_selected(ncand, T, need_eq, m, list, out, scratch, [&](int c, uint32_t* key, int* slot) {
+      *key = ckey[c];
+      *slot = cslot[c];
+    });
+  } else {
+    emit_selected(n, T, need_eq, m, list, out, scratch, [&](int c, uint32_t* key, int* slot) {
+      *key = score_key(row[c]);
+      *slot = c;
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Top-m of short rows (n <= 4096, e.g. a member's candidates): one wave per
+// row.  The row's keys live in registers (64 per lane), the radix select runs
+// four 8-bit digits against a private 256-bin LDS histogram per wave, and the
+// index-ordered emission is a wave-level scan, so no workgroup barrier is
+// needed.  Lane l holds elements 256*i + 4*l .. 256*i + 4*l + 3 of chunk i.
+// ---------------------------------------------------------------------------
+constexpr int kSmallMax = 4096;
+constexpr int kSmallWaves = 4;
+constexpr int kSmallChunks = kSmallMax / 256;
+
+__device__ inline uint32_t wave_exclusive_sum(uint32_t v, uint32_t* total) {
+  const uint32_t inc = wave_inclusive_sum(v);
+  *total = __shfl(inc, 63, 64);
+  return inc - v;
+}
+
+// Orders this wave's LDS accesses across lanes (wave-scope fence + barrier).
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArgs a) {
+  __shared__ uint32_t hist_all[kSmallWaves][256];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int i = blockIdx.x * kSmallWaves + wid;
+  if (i >= a.nrows) return;
+  uint32_t* hist = hist_all[wid];
+  const int R = a.row_begin + i;
+  const float* row = a.S + (long long)i * a.ldS;
+  int32_t* out = a.out + (long long)i * a.ldo;
+  const int32_t* list;
+  const int n = row_length(a, R, &list);
+  const uint32_t m = (uint32_t)a.m;
+  if (n <= (int)m) {
+    for (int s = lane; s < (int)m; s += kWave) out[s] = s < n ? (list ? list[s] : s) : -1;
+    return;
+  }
+
+  // keys and output values (candidate positions, or the slots themselves) of
+  // this lane's elements, all loaded up front
+  uint32_t key[kSmallChunks * 4];
+  int32_t val[kSmallChunks * 4];
+  const bool list16 = list && ((uintptr_t)list & 15u) == 0;  // 16-byte loads of the list
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int s0 = c * 256 + lane * 4;
+    const float4 v = load4(row, s0, n);
+    i32x4 p = i32x4{s0, s0 + 1, s0 + 2, s0 + 3};
+    if (list) {
+      if (list16 && s0 + 3 < n) {
+        p = *reinterpret_cast<const i32x4*>(list + s0);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = s0 + e < n ? list[s0 + e] : -1;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[c * 4 + e] = score_key(f4(v, e));
+      val[c * 4 + e] = p[e];
+    }
+  }
+  auto valid = [&](int c, int e) { return c * 256 + lane * 4 + e < n; };
+
+  // bits above the highest bit where the row's keys differ are common to all
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (valid(c, e)) {
+        kmin = min(kmin, key[c * 4 + e]);
+        kmax = max(kmax, key[c * 4 + e]);
+      }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+  }
+  int top = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));  // undetermined low bits
+  uint32_t pmask = top == 32 ? 0u : ~0u << top;
+  uint32_t prefix = kmax & pmask, rem = m;
+  while (top > 0) {
+    const int width = top < 8 ? top : 8;
+    const int shift = top - width;
+    const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0u;
+    wave_sync();
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (valid(c, e) && (key[c * 4 + e] & pmask) == prefix)
+          atomicAdd(&hist[(key[c * 4 + e] >> shift) & dmask], 1u);
+    wave_sync();
+    // lane l owns bins 255-4l .. 252-4l (descending)
+    uint32_t cnt[4], sum = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      cnt[b] = hist[255 - lane * 4 - b];
+      sum += cnt[b];
+    }
+    uint32_t tot;
+    uint32_t run = wave_exclusive_sum(sum, &tot);
+    int found = -1;
+    uint32_t above = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (found < 0 && run < rem && rem <= run + cnt[b]) {
+        found = 255 - lane * 4 - b;
+        above = run;
+      }
+      run += cnt[b];
+    }
+    const unsigned long long hit = __ballot(found >= 0);
+    const int src = hit ? __ffsll((long long)hit) - 1 : 0;
+    const uint32_t digit = (uint32_t)__shfl(found, src, 64);
+    above = __shfl(above, src, 64);
+    prefix |= digit << shift;
+    pmask |= dmask << shift;
+    rem -= above;
+    top = shift;
+    wave_sync();
+  }
+  const uint32_t T = prefix, need_eq = rem, need_gt = m - rem;
+
+  uint32_t g_gt = 0, g_eq = 0;
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool v = valid(c, e);
+      cgt += (v && key[c * 4 + e] > T) ? 1u : 0u;
+      ceq += (v && key[c * 4 + e] == T) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t excl = wave_exclusive_sum(cgt | (ceq << 16), &tot);
+    uint32_t gt_before = g_gt + (excl & 0xFFFFu), eq_before = g_eq + (excl >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!valid(c, e)) continue;
+      const uint32_t kk = key[c * 4 + e];
+      if (kk > T) {
+        const uint32_t p = gt_before + min(eq_before, need_eq);
+        if (p < m) out[p] = val[c * 4 + e];
+        ++gt_before;
+      } else if (kk == T) {
+        const uint32_t p = gt_before + eq_before;
+        if (eq_before < need_eq && p < m) out[p] = val[c * 4 + e];
+        ++eq_before;
+      }
+    }
+    g_gt += tot & 0xFFFFu;
+    g_eq += tot >> 16;
+  }
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.nrows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(a.nrows), dim3(kTopkThreads), 0, st, a);
+  // rows whose length is bounded by the candidate list (Refine) fit one wave
+  const bool small = a.kind == kLenRefine && a.ldmap <= kSmallMax;
+  if (small)
+    hipLaunchKernelGGL(topk_small_kernel, dim3((a.nrows + kSmallWaves - 1) / kSmallWaves),
+                       dim3(kSmallWaves * kWave), 0, st, a);
+  else
+    hipLaunchKernelGGL(topk_kernel, dim3(a.nrows), dim3(kTopkThreads), 0, st, a);
   return hipGetLastError();
 }
 
