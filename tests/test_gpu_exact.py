@@ -233,6 +233,24 @@ def test_decode_exact(mode):
         assert np.array_equal(out[b], ref), b
 
 
+@pytest.mark.parametrize("dtype,mode", [("bf16", "dense"), ("bf16", "refine"), ("fp8", "refine")])
+def test_decode_exact_many_sequences(dtype, mode):
+    # about 1100 key pairs over the batch: the decode scan's per-workgroup
+    # runs of pairs start and end inside sequences and span several of them
+    print(f"case: decode exact B=24 H=64 D=128 {dtype} {mode}", flush=True)
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(2, 6000, 24)]
+    lens[3], lens[7], lens[8], lens[9] = 6000, 64, 65, 2
+    dec = _decode_inputs(24, lens, g=2, H=64, D=128, dtype=dtype, Lmax=6000, seed=22)
+    d = to_device(dec)
+    kw = dict(q_scale=d["q_scale"], k_scale=d["k_scale"]) if dtype == "fp8" else {}
+    out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=64, C=256, mode=mode,
+                            **kw).cpu().numpy()
+    for b in range(24):
+        ref, _, _ = oracle.decode_seq(dec, b, 64, 256, mode)
+        assert np.array_equal(out[b], ref), b
+
+
 def test_decode_matches_last_prefill_group_and_rejects_bad_lengths():
     print("case: decode == last prefill group; invalid cache lengths give -1 rows", flush=True)
     g = 4

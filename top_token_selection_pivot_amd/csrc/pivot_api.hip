@@ -30,7 +30,6 @@ int fail(int status, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreBudget = size_t(1) << 30;  // preferred score bytes per pass
 constexpr int kScanKeyChunk = 2048;              // keys per scan workgroup
-constexpr int kDecodeKeyChunk = 1024;            // keys per decode-scan workgroup
 constexpr int kRefineSlotChunk = 1024;           // candidate slots per refine workgroup
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -284,8 +283,11 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
 // ---------------------------------------------------------------------------
 struct DecodePlan {
   int m;
+  int rows;   // scored rows: B proxies, or B*g members for DENSE
+  int parts;  // workgroups per row in the decode top-m gather
   long long ldS, ldR;
-  size_t off_qbar, off_qs, off_wbar, off_cand, off_S, off_R, total;
+  size_t off_qbar, off_qs, off_wbar, off_cand, off_S, off_R, off_hist, off_ckey, off_cslot, off_ccount,
+      total;
 };
 
 DecodePlan plan_decode(int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
@@ -308,6 +310,16 @@ DecodePlan plan_decode(int B, int Lmax, int H, int D, int g, int topk, int C, in
   off = align_up(off + (size_t)B * (dense ? g : 1) * p.ldS * 4);
   p.off_R = off;
   if (mode == PIVOT_MODE_REFINE) off = align_up(off + (size_t)B * g * p.ldR * 4);
+  p.rows = dense ? B * g : B;
+  p.parts = (int)std::min<long long>(32, std::max<long long>(1, (Lmax + 4095) / 4096));
+  p.off_hist = off;
+  off = align_up(off + (size_t)p.rows * kSelectBins1 * 4);
+  p.off_ckey = off;
+  off = align_up(off + (size_t)p.rows * p.parts * kSelectCap * 4);
+  p.off_cslot = off;
+  off = align_up(off + (size_t)p.rows * p.parts * kSelectCap * 4);
+  p.off_ccount = off;
+  off = align_up(off + (size_t)p.rows * p.parts * 4);
   p.total = off;
   return p;
 }
@@ -416,22 +428,20 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   const uint8_t* kb = (const uint8_t*)k_cache;
   float* S = (float*)(ws + p.off_S);
 
+  uint32_t* hist = (uint32_t*)(ws + p.off_hist);
+  DecSelectArgs sel{S, p.ldS, p.rows, 0, 0, g, Lmax, cache_len, hist, p.parts,
+                    (uint32_t*)(ws + p.off_ckey), (int32_t*)(ws + p.off_cslot), (int32_t*)(ws + p.off_ccount),
+                    nullptr, 0};
+  PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_fill_u32(hist, (size_t)p.rows * kSelectBins1, 0u, s),
+                 "decode histogram clear");
   if (mode == PIVOT_MODE_DENSE) {
-    DecScanArgs da{qb, q_scale, w, kb, k_scale, Lmax, H, cache_len, g, g, kDecodeKeyChunk, S, p.ldS};
-    PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, B, s), "decode scan");
-    TopkArgs ta{};
-    ta.S = S;
-    ta.ldS = p.ldS;
-    ta.row_begin = 0;
-    ta.nrows = B * g;
-    ta.m = topk;
-    ta.out = out;
-    ta.ldo = topk;
-    ta.kind = kLenDecodeDense;
-    ta.g = g;
-    ta.Lmax = Lmax;
-    ta.cache_len = cache_len;
-    PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "decode dense top-k");
+    DecScanArgs da{qb, q_scale, w, kb, k_scale, Lmax, H, cache_len, g, g, S, p.ldS, hist, B};
+    PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");
+    sel.m = topk;
+    sel.kind = kLenDecodeDense;
+    sel.out = out;
+    sel.ldo = topk;
+    PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_decode_select(sel, s), "decode dense top-k");
     return PIVOT_OK;
   }
   uint8_t* qbar = ws + p.off_qbar;
@@ -440,21 +450,13 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   int32_t* cand = cand_user ? cand_user : (int32_t*)(ws + p.off_cand);
   ProxyArgs pa{qb, q_scale, w, B * g, H, D, g, qbar, qbs, wbar};
   PIVOT_LAUNCH_K(PIVOT_K_PROXY, s, launch_proxy_mean(pa, dtype, s), "decode proxy mean");
-  DecScanArgs da{qbar, qbs, wbar, kb, k_scale, Lmax, H, cache_len, g, 1, kDecodeKeyChunk, S, p.ldS};
-  PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, B, s), "decode scan");
-  TopkArgs ta{};
-  ta.S = S;
-  ta.ldS = p.ldS;
-  ta.row_begin = 0;
-  ta.nrows = B;
-  ta.m = p.m;
-  ta.out = cand;
-  ta.ldo = p.m;
-  ta.kind = kLenCache;
-  ta.g = g;
-  ta.Lmax = Lmax;
-  ta.cache_len = cache_len;
-  PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "decode proxy top-m");
+  DecScanArgs da{qbar, qbs, wbar, kb, k_scale, Lmax, H, cache_len, g, 1, S, p.ldS, hist, B};
+  PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");
+  sel.m = p.m;
+  sel.kind = kLenCache;
+  sel.out = cand;
+  sel.ldo = p.m;
+  PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_decode_select(sel, s), "decode proxy top-m");
   if (cand_user) return PIVOT_OK;
   if (mode == PIVOT_MODE_REUSE) {
     BroadcastArgs ba{cand, p.m, 0, out, topk, 1, g, Lmax, cache_len, 0, B * g};

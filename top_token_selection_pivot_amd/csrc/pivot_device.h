@@ -77,6 +77,39 @@ __device__ inline typename Fmt<DT>::frag zero_frag() {
   return typename Fmt<DT>::frag{};
 }
 
+// s_waitcnt immediate that waits for every vector-memory operation of the
+// wave (vmcnt 0) and leaves the export and LDS/scalar counters unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Direct-to-LDS buffer loads: lane l's 16 (or 4) bytes from voffset land at
+// LDS byte address lds + 16*l (4*l); reads past the buffer's range write zeros.
+// They are issued as inline assembly, outside the compiler's wait tracking, so
+// the caller waits for them explicitly (lds_dma_wait) before reading the
+// destination.  Nothing else in the kernels that use them reads M0.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+__device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+// Wait until at most N vector-memory operations of the wave are outstanding
+// (they complete in issue order); a compiler barrier for memory accesses.
+template <int N>
+__device__ inline void lds_dma_wait() {
+  static_assert(N >= 0 && N < 64);
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Byte offset, inside one D-row, of the fragment of step ks for lane half hf.
 template <int DT, int D>
 __device__ constexpr int frag_offset(int ks, int hf) {

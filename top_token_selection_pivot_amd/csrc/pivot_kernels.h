@@ -61,6 +61,9 @@ struct RefineArgs {
 // Decode scan: for each sequence b, qr query rows (rows b*qr .. b*qr+qr-1 of
 // q) scan the sequence's cache_len[b] keys.  qr == 1: the proxy, which sees
 // every key; otherwise the g members, member i seeing keys 0..n_b-g+i.
+// Each workgroup takes (sequence, chunk of kDecChunk keys) work items; `hist`
+// (optional, zeroed beforehand) receives for every output row the histogram of
+// the top 12 bits of its scores' order-preserving keys, [B*qr][4096].
 struct DecScanArgs {
   const uint8_t* q;
   const float* q_scale;
@@ -70,9 +73,31 @@ struct DecScanArgs {
   int Lmax, H;
   const int32_t* cache_len;
   int g, qr;
-  int kc;
   float* S;
   long long ldS;
+  uint32_t* hist;
+  int B;
+};
+
+// Top-m of decode score rows with precomputed first-digit histograms: `parts`
+// workgroups per row gather the keys at or above the threshold bin of their
+// slice into per-slice regions ([nrows][parts][kTopkCap] keys and slots,
+// counts [nrows][parts], -1 if the threshold bin is too crowded), then one
+// workgroup per row finishes the selection.
+struct DecSelectArgs {
+  const float* S;
+  long long ldS;
+  int nrows, m;
+  int kind;  // kLenCache or kLenDecodeDense
+  int g, Lmax;
+  const int32_t* cache_len;
+  const uint32_t* hist;
+  int parts;
+  uint32_t* ckey;
+  int32_t* cslot;
+  int32_t* ccount;
+  int32_t* out;
+  long long ldo;
 };
 
 // Row-length rules of the top-m selection.
@@ -114,10 +139,16 @@ struct BroadcastArgs {
 hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_refine(const RefineArgs& a, int dtype, int D, hipStream_t st);
-hipError_t launch_decode_scan(const DecScanArgs& a, int dtype, int D, int B, hipStream_t st);
+hipError_t launch_decode_scan(const DecScanArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_broadcast(const BroadcastArgs& a, hipStream_t st);
 hipError_t launch_selftest_mfma(int32_t* out, hipStream_t st);
+hipError_t launch_decode_select(const DecSelectArgs& a, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
+
+constexpr int kDecChunk = 2048;      // keys per decode-scan work item
+constexpr int kSelectCap = 7680;     // keys a long-row selection stages in LDS
+constexpr int kSelectBins1 = 4096;   // bins of the first radix digit (top 12 bits)
 
 bool score_shape_supported(int dtype, int D);
 

@@ -16,7 +16,8 @@
 //                        of one group score the group's candidate keys,
 //                        gathered from the key cache through its candidate list.
 //  * decode_scan_kernel: one sequence's 1-2 query rows stream that sequence's
-//                        key cache straight into registers (no reuse to stage).
+//                        key cache through per-wave LDS rings filled by
+//                        direct-to-LDS loads (no reuse across rows to stage).
 #pragma once
 
 #include "pivot_device.h"
@@ -175,18 +176,18 @@ __device__ inline void sched_tile_step() {
 
 constexpr int kScanWaveThreads = kScanRows * kWave;
 
-// Geometry of one workgroup of the scoring loop: its query rows, the key
-// positions it covers and where scores go.
-//  * full-prefix scan (GATHER = false, ScanArgs): rows rb..rb+7, a chunk of
+// Geometry of one workgroup of the scoring loop (ROWS waves, one query row
+// each): its query rows, the key positions it covers and where scores go.
+//  * full-prefix scan (GATHER = false, ScanArgs): rows rb..rb+ROWS-1, a chunk of
 //    contiguous keys [k0, k1); row r keeps keys <= pos(r).
 //  * Refine (GATHER = true, RefineArgs): the members of one group, a chunk of
 //    candidate slots [k0, k1) whose keys are gathered through the group's
 //    candidate list; every slot < the group's candidate count is kept.
-template <int DT, int D, int HB, bool GATHER, typename Args>
-__global__ __launch_bounds__(kScanWaveThreads) void score_block_kernel(Args a) {
+template <int DT, int D, int HB, bool GATHER, int ROWS, typename Args>
+__global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
   using KT = KeyTile<DT, D>;
   using Frag = typename Fmt<DT>::frag;
-  constexpr int NT = kScanWaveThreads;
+  constexpr int NT = ROWS * kWave;
   constexpr int NKS = D / Fmt<DT>::KSTEP;
   constexpr int SCH = kStageTiles * KT::CHUNKS;  // 16-byte pieces per stage
   constexpr int NPT = (SCH + NT - 1) / NT;
@@ -209,8 +210,8 @@ __global__ __launch_bounds__(kScanWaveThreads) void score_block_kernel(Args a) {
   __amdgpu_buffer_rsrc_t crs; // Refine: candidate positions of slots [k0, k1)
   __amdgpu_buffer_rsrc_t ksr; // fp8 key scales (empty for bf16)
   if constexpr (!GATHER) {
-    const int rb = a.row_begin + blockIdx.y * kScanRows;
-    const int rlast = min(rb + kScanRows, a.row_end) - 1;
+    const int rb = a.row_begin + blockIdx.y * ROWS;
+    const int rlast = min(rb + ROWS, a.row_end) - 1;
     const int lim = min(rlast * a.pos_mul + a.pos_add, a.pos_cap) + 1;  // keys 0..lim-1
     k0 = blockIdx.x * a.kc;
     if (k0 >= lim) return;
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kScanWaveThreads) void score_block_kernel(Args a) {
     k0 = blockIdx.x * a.slot_chunk;
     if (k0 >= ncand) return;
     k1 = min(k0 + a.slot_chunk, ncand);
-    const int mem = blockIdx.z * kScanRows + wid;
+    const int mem = blockIdx.z * ROWS + wid;
     active = mem < nmem;
     r = row0 + (active ? mem : 0);
     nvalid = active ? k1 : 0;
@@ -366,59 +367,206 @@ __global__ __launch_bounds__(kScanWaveThreads) void score_block_kernel(Args a) {
 
 // ---------------------------------------------------------------------------
 // Decode scan: QR query rows of one sequence stream its key cache.
+//
+// The batch's keys are cut into pairs of 32-key tiles, sequence by sequence,
+// and every workgroup takes an equal run of consecutive pairs (a run spans at
+// most a few sequences).  Inside a run each wave streams every W-th pair
+// through a ring of R stages of its own in LDS, filled by direct-to-LDS buffer
+// loads (no registers held by loads in flight): while one stage is contracted
+// the other R-1 are loading.  A stage is written in 1 KB wave-wide pieces,
+// 16 bytes per lane, with the 16-byte chunks of each key row XOR-swizzled by
+// the row index so that the fragment reads of 32 rows spread over the banks.
+// The buffer range ends at the run's last key (reads beyond it return zero,
+// stores beyond a row's causal limit are dropped).  The scores are written,
+// and the top 12 bits of their keys are histogrammed per row in LDS and added
+// to the row's histogram in memory whenever the run moves to the next
+// sequence.
 // ---------------------------------------------------------------------------
-constexpr int kDecThreads = 256;
+template <int DT, int D, int QR>
+struct DecGeom {
+  static constexpr int ROW = D * Fmt<DT>::ESZ;            // bytes of one key row
+  static constexpr int PAIR_KEYS = 2 * kTileN;
+  static constexpr int PAIR_BYTES = PAIR_KEYS * ROW;
+  static constexpr int STAGE_BYTES = PAIR_BYTES + (DT == kFP8 ? PAIR_KEYS * 4 : 0);  // + key scales
+  static constexpr int FIXED = QR * kSelectBins1 * 4 + 1024;
+  static constexpr bool fits(int w, int r) { return r * w * STAGE_BYTES + FIXED <= 150 * 1024; }
+  static constexpr int LOADS = PAIR_BYTES / 1024;         // wave-wide 1 KB pieces per pair
+  static constexpr int STAGE_OPS = LOADS + (DT == kFP8 ? 1 : 0);  // loads that fill one stage
+  static constexpr int W = (fits(4, 3) || fits(4, 2)) ? 4 : (fits(2, 3) || fits(2, 2)) ? 2 : 1;
+  // a wait names the newer stages' loads in a 6-bit count
+  static constexpr int R = (fits(W, 3) && 2 * STAGE_OPS < 64) ? 3 : 2;
+  static constexpr int THREADS = W * kWave;
+  static constexpr int CPR = ROW / 16;                    // 16-byte chunks per key row
+  static constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;     // swizzle mask
+  static_assert(PAIR_BYTES % 1024 == 0 && fits(W, R) && (R - 1) * STAGE_OPS < 64);
+};
 
 template <int DT, int D, int HB, int QR>
-__global__ __launch_bounds__(kDecThreads) void decode_scan_kernel(DecScanArgs a) {
-  constexpr int NKS = D / Fmt<DT>::KSTEP;
-  constexpr int ROW = D * Fmt<DT>::ESZ;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int b = blockIdx.y;
-  const int nb = a.cache_len[b];
-  if (nb < a.g || nb > a.Lmax) return;
-  const int k0 = blockIdx.x * a.kc;
-  if (k0 >= nb) return;
-  const int k1 = min(k0 + a.kc, nb);
-
-  // rows of this workgroup: qr rows per sequence, QR at a time (blockIdx.z)
+__global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_kernel(DecScanArgs a) {
+  using G = DecGeom<DT, D, QR>;
+  using Frag = typename Fmt<DT>::frag;
+  constexpr int ROW = G::ROW, W = G::W, R = G::R, NT = G::THREADS;
+  constexpr int NB = kSelectBins1;
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[W][G::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[W][G::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[R > 2 ? W : 1][R > 2 ? G::STAGE_BYTES : 16];
+  __shared__ uint32_t hist[QR][NB];
+  __shared__ uint32_t scratch[NT / kWave + 1];
+  __shared__ int sh_b, sh_off;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, n = lane & 31;
   const int ri0 = blockIdx.z * QR;
-  QueryRegs<DT, D, HB> q[QR];
-  float qs[QR];
-  int pos[QR];
-#pragma unroll
-  for (int i = 0; i < QR; ++i) {
-    const int ri = ri0 + i;
-    pos[i] = -1;
-    qs[i] = 1.f;
-    if (ri < a.qr) {
-      const size_t row = (size_t)b * a.qr + ri;
-      q[i].load(a.q + row * a.H * ROW, a.w + row * a.H, a.H, lane);
-      if constexpr (DT == kFP8) qs[i] = a.q_scale[row];
-      pos[i] = a.qr == 1 ? nb - 1 : nb - a.g + ri;
+
+  auto seq_pairs = [&](int b) -> uint32_t {
+    const int nb = a.cache_len[b];
+    return (nb < a.g || nb > a.Lmax) ? 0u : (uint32_t)(nb + G::PAIR_KEYS - 1) / G::PAIR_KEYS;
+  };
+  // this workgroup's run [lo, hi) of the batch's pairs, and where it starts
+  uint32_t total = 0;
+  for (int b0 = 0; b0 < a.B; b0 += NT) {
+    uint32_t tot;
+    block_exclusive_sum<NT>(b0 + tid < a.B ? seq_pairs(b0 + tid) : 0u, scratch, &tot);
+    total += tot;
+  }
+  const uint32_t lo = (uint32_t)((uint64_t)total * blockIdx.x / gridDim.x);
+  const uint32_t hi = (uint32_t)((uint64_t)total * (blockIdx.x + 1) / gridDim.x);
+  if (lo == hi) return;
+  {
+    uint32_t base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += NT) {
+      const int b = b0 + tid;
+      const uint32_t p = b < a.B ? seq_pairs(b) : 0u;
+      uint32_t tot;
+      const uint32_t ex = block_exclusive_sum<NT>(p, scratch, &tot);
+      if (p && base + ex <= lo && lo < base + ex + p) {
+        sh_b = b;
+        sh_off = (int)(lo - base - ex);
+      }
+      base += tot;
+      if (base > lo) break;
     }
   }
-  const uint8_t* kb = a.k + (size_t)b * a.Lmax * ROW;
-  const float* ksc = a.k_scale + (DT == kFP8 ? (size_t)b * a.Lmax : 0);
-  const int hf = lane >> 5, n = lane & 31;
+  for (int i = 0; i < QR; ++i)
+    for (int e = tid; e < NB; e += NT) hist[i][e] = 0u;
+  __syncthreads();
+  int b = sh_b, off = sh_off;
+  uint32_t left = hi - lo;
 
-  for (int t0 = k0 + wid * kTileN; t0 < k1; t0 += (kDecThreads / kWave) * kTileN) {
-    const int key = min(t0 + n, k1 - 1);
-    typename Fmt<DT>::frag bf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      bf[ks] = load_frag<DT>(kb + (size_t)key * ROW + frag_offset<DT, D>(ks, hf));
-    float ksv = 1.f;
-    if constexpr (DT == kFP8) ksv = ksc[min(t0 + lane, k1 - 1)];
+  while (left > 0 && b < a.B) {
+    const int nb = a.cache_len[b];
+    const int np = (int)min((uint32_t)((nb + G::PAIR_KEYS - 1) / G::PAIR_KEYS - off), left);
+    const int k0 = off * G::PAIR_KEYS;
+    const int k1 = min(k0 + np * G::PAIR_KEYS, nb);
+
+    QueryRegs<DT, D, HB> q[QR];
+    float qs[QR];
+    int pos[QR];
+    __amdgpu_buffer_rsrc_t srs[QR];
 #pragma unroll
     for (int i = 0; i < QR; ++i) {
-      if (pos[i] < 0 || t0 > pos[i]) continue;
-      float s = score_tile<DT, D, HB>(q[i], [&](int ks) { return bf[ks]; });
-      const int kk = t0 + lane;
-      if (lane < kTileN && kk <= pos[i] && kk < k1) {
-        if constexpr (DT == kFP8) s = (s * qs[i]) * ksv;
-        a.S[((size_t)b * a.qr + ri0 + i) * a.ldS + kk] = s;
+      const int ri = ri0 + i;
+      pos[i] = -1;
+      qs[i] = 1.f;
+      if (ri < a.qr) {
+        const size_t rowi = (size_t)b * a.qr + ri;
+        q[i].load(a.q + rowi * a.H * ROW, a.w + rowi * a.H, a.H, lane);
+        if constexpr (DT == kFP8) qs[i] = a.q_scale[rowi];
+        pos[i] = a.qr == 1 ? nb - 1 : nb - a.g + ri;
       }
+      const int nvalid = pos[i] < 0 ? 0 : min(pos[i] + 1, k1);
+      srs[i] = make_rsrc(a.S + ((size_t)b * a.qr + (pos[i] < 0 ? 0 : ri)) * a.ldS, (uint32_t)nvalid * 4u);
+    }
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + ((size_t)b * a.Lmax + k0) * ROW, (uint32_t)(k1 - k0) * ROW);
+    const __amdgpu_buffer_rsrc_t ksr =
+        make_rsrc(DT == kFP8 ? a.k_scale + (size_t)b * a.Lmax + k0 : a.w, DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u);
+
+    // the query registers are complete before the ring starts
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // wave-local pair s is the run's pair wid + W*s, held by stage s % R
+    auto issue = [&](const uint8_t* stage, int s) {
+      const int key0 = (wid + W * s) * G::PAIR_KEYS;
+      const uint32_t dst = lds_addr(stage);
+#pragma unroll
+      for (int c = 0; c < G::LOADS; ++c) {
+        const int slot = c * kWave + lane;
+        const int kr = slot / G::CPR;
+        const int chunk = (slot % G::CPR) ^ (kr & G::SWM);
+        lds_dma16(krs, dst + c * 1024, (uint32_t)((key0 + kr) * ROW + chunk * 16));
+      }
+      if constexpr (DT == kFP8) lds_dma4(ksr, dst + G::PAIR_BYTES, (uint32_t)((key0 + lane) * 4));
+    };
+    // a stage is complete once at most the R-1 newer stages' loads (and
+    // any score stores issued after it) are outstanding
+    constexpr int kStageOps = G::STAGE_OPS;
+    auto frag_at = [&](const uint8_t* stage, int t, int ks) -> Frag {
+      const int kr = t * kTileN + n;
+      const int c0 = frag_offset<DT, D>(ks, hf) / 16;
+      const uint8_t* row = stage + kr * ROW;
+      if constexpr (DT == kBF16) {
+        return *reinterpret_cast<const i32x4*>(row + ((c0 ^ (kr & G::SWM)) << 4));
+      } else {
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(row + ((c0 ^ (kr & G::SWM)) << 4));
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(row + (((c0 + 1) ^ (kr & G::SWM)) << 4));
+        return i32x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+    };
+    auto compute = [&](const uint8_t* stage, int s) {
+      const int key = k0 + (wid + W * s) * G::PAIR_KEYS + lane;
+      float ksv = 1.f;
+      if constexpr (DT == kFP8) ksv = *reinterpret_cast<const float*>(stage + G::PAIR_BYTES + 4 * lane);
+#pragma unroll
+      for (int i = 0; i < QR; ++i) {
+        if (pos[i] < 0) continue;
+        TileAcc<HB> acc0, acc1;
+        mma_tile<DT, D, HB>(q[i], [&](int ks) { return frag_at(stage, 0, ks); }, acc0);
+        mma_tile<DT, D, HB>(q[i], [&](int ks) { return frag_at(stage, 1, ks); }, acc1);
+        float sc = pair_combine(tile_partial<DT, D, HB>(q[i], acc0), tile_partial<DT, D, HB>(q[i], acc1));
+        if constexpr (DT == kFP8) sc = (sc * qs[i]) * ksv;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srs[i], key * 4, 0, 0);
+        if (a.hist && key < k1 && key <= pos[i]) atomicAdd(&hist[i][score_key(sc) >> 20], 1u);
+      }
+    };
+
+    // loads past the wave's last pair fall beyond the run and write zeros
+    const int npw = np > wid ? (np - wid + W - 1) / W : 0;
+    issue(ring0[wid], 0);
+    issue(ring1[wid], 1);
+    if constexpr (R > 2) issue(ring2[wid], 2);
+    for (int s = 0; s < npw; s += R) {
+      lds_dma_wait<(R - 1) * kStageOps>();
+      compute(ring0[wid], s);
+      issue(ring0[wid], s + R);
+      lds_dma_wait<(R - 1) * kStageOps>();
+      if (s + 1 < npw) compute(ring1[wid], s + 1);
+      issue(ring1[wid], s + 1 + R);
+      if constexpr (R > 2) {
+        lds_dma_wait<(R - 1) * kStageOps>();
+        if (s + 2 < npw) compute(ring2[wid], s + 2);
+        issue(ring2[wid], s + 2 + R);
+      }
+    }
+    // every load of this wave has landed before its stages are refilled
+    lds_dma_wait<0>();
+    __syncthreads();
+    if (a.hist) {
+      for (int i = 0; i < QR; ++i) {
+        if (pos[i] < 0) continue;
+        uint32_t* gh = a.hist + ((size_t)b * a.qr + ri0 + i) * NB;
+        for (int e = tid; e < NB; e += NT) {
+          const uint32_t v = hist[i][e];
+          if (v) {
+            atomicAdd(&gh[e], v);
+            hist[i][e] = 0u;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    left -= (uint32_t)np;
+    off = 0;
+    while (left > 0 && ++b < a.B && seq_pairs(b) == 0) {
     }
   }
 }

@@ -8,18 +8,44 @@ namespace pivot {
 
 template <int DT, int D, int HB>
 static void scan_one(const ScanArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((score_block_kernel<DT, D, HB, false, ScanArgs>), grid, dim3(kScanWaveThreads), 0, st, a);
+  hipLaunchKernelGGL((score_block_kernel<DT, D, HB, false, kScanRows, ScanArgs>), grid, dim3(kScanRows * kWave), 0,
+                     st, a);
 }
+// Refine workgroups have as many waves as a group has members (2, 4 or 8).
 template <int DT, int D, int HB>
-static void refine_one(const RefineArgs& a, dim3 grid, dim3 block, hipStream_t st) {
-  hipLaunchKernelGGL((score_block_kernel<DT, D, HB, true, RefineArgs>), grid, dim3(kScanWaveThreads), 0, st, a);
-}
-template <int DT, int D, int HB>
-static void decode_one(const DecScanArgs& a, dim3 grid, hipStream_t st) {
-  if (a.qr == 1)
-    hipLaunchKernelGGL((decode_scan_kernel<DT, D, HB, 1>), grid, dim3(kDecThreads), 0, st, a);
+static void refine_one(const RefineArgs& a, dim3 grid, int rows, hipStream_t st) {
+  if (rows == 2)
+    hipLaunchKernelGGL((score_block_kernel<DT, D, HB, true, 2, RefineArgs>), grid, dim3(2 * kWave), 0, st, a);
+  else if (rows == 4)
+    hipLaunchKernelGGL((score_block_kernel<DT, D, HB, true, 4, RefineArgs>), grid, dim3(4 * kWave), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_scan_kernel<DT, D, HB, 2>), grid, dim3(kDecThreads), 0, st, a);
+    hipLaunchKernelGGL((score_block_kernel<DT, D, HB, true, 8, RefineArgs>), grid, dim3(8 * kWave), 0, st, a);
+}
+// Decode scan workgroups are persistent: as many as fit on the chip at once.
+template <int DT, int D, int HB, int QR>
+static void decode_launch(const DecScanArgs& a, int zblocks, hipStream_t st) {
+  using G = DecGeom<DT, D, QR>;
+  static const int per_cu = [] {
+    int nblk = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, decode_scan_kernel<DT, D, HB, QR>, G::THREADS, 0) !=
+            hipSuccess ||
+        nblk < 1)
+      nblk = 1;
+    return nblk;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus < 1)
+    cus = 1;
+  dim3 grid(cus * per_cu, 1, zblocks);
+  hipLaunchKernelGGL((decode_scan_kernel<DT, D, HB, QR>), grid, dim3(G::THREADS), 0, st, a);
+}
+template <int DT, int D, int HB>
+static void decode_one(const DecScanArgs& a, int zblocks, hipStream_t st) {
+  if (a.qr == 1)
+    decode_launch<DT, D, HB, 1>(a, zblocks, st);
+  else
+    decode_launch<DT, D, HB, 2>(a, zblocks, st);
 }
 
 // Calls f.operator()<D, HB>() for the supported head-dimension / head-block combination.
@@ -55,20 +81,24 @@ hipError_t launch_scan_dt(const ScanArgs& a, int D, hipStream_t st) {
 }
 
 template <int DT>
-hipError_t launch_refine_dt(const RefineArgs& a, int D, hipStream_t st) {
+hipError_t launch_refine_dt(const RefineArgs& a_in, int D, hipStream_t st) {
+  RefineArgs a = a_in;
   const int ngrp = a.grp_end - a.grp_begin;
-  dim3 grid((a.m + a.slot_chunk - 1) / a.slot_chunk, ngrp, (a.g + kScanRows - 1) / kScanRows);
-  dim3 block(kScanWaveThreads);
-  auto f = [&]<int D_, int HB_>() { refine_one<DT, D_, HB_>(a, grid, block, st); };
+  const int rows = a.g <= 2 ? 2 : a.g <= 4 ? 4 : kScanRows;
+  const int zblocks = (a.g + rows - 1) / rows;
+  // all candidates in one workgroup when there are enough groups to fill the
+  // chip (each member's query is then loaded once); 256-slot pieces otherwise
+  a.slot_chunk = (long long)ngrp * zblocks >= 2048 ? a.m : 256;
+  dim3 grid((a.m + a.slot_chunk - 1) / a.slot_chunk, ngrp, zblocks);
+  auto f = [&]<int D_, int HB_>() { refine_one<DT, D_, HB_>(a, grid, rows, st); };
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_decode_scan_dt(const DecScanArgs& a, int D, int B, hipStream_t st) {
-  const int qr_step = a.qr == 1 ? 1 : 2;
-  dim3 grid((a.Lmax + a.kc - 1) / a.kc, B, (a.qr + qr_step - 1) / qr_step);
-  auto f = [&]<int D_, int HB_>() { decode_one<DT, D_, HB_>(a, grid, st); };
+hipError_t launch_decode_scan_dt(const DecScanArgs& a, int D, hipStream_t st) {
+  const int zblocks = a.qr == 1 ? 1 : (a.qr + 1) / 2;
+  auto f = [&]<int D_, int HB_>() { decode_one<DT, D_, HB_>(a, zblocks, st); };
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -1,5 +1,7 @@
 // pivot_select.hip -- proxy mean, top-m selection, Reuse broadcast and the
 // matrix-core layout self-test (gfx950).
+#include <algorithm>
+
 #include "pivot_device.h"
 #include "pivot_kernels.h"
 
@@ -9,8 +11,8 @@ hipError_t launch_scan_bf16(const ScanArgs&, int, hipStream_t);
 hipError_t launch_scan_fp8(const ScanArgs&, int, hipStream_t);
 hipError_t launch_refine_bf16(const RefineArgs&, int, hipStream_t);
 hipError_t launch_refine_fp8(const RefineArgs&, int, hipStream_t);
-hipError_t launch_decode_scan_bf16(const DecScanArgs&, int, int, hipStream_t);
-hipError_t launch_decode_scan_fp8(const DecScanArgs&, int, int, hipStream_t);
+hipError_t launch_decode_scan_bf16(const DecScanArgs&, int, hipStream_t);
+hipError_t launch_decode_scan_fp8(const DecScanArgs&, int, hipStream_t);
 
 hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st) {
   return dtype == kBF16 ? launch_scan_bf16(a, D, st) : launch_scan_fp8(a, D, st);
@@ -18,9 +20,9 @@ hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st) {
 hipError_t launch_refine(const RefineArgs& a, int dtype, int D, hipStream_t st) {
   return dtype == kBF16 ? launch_refine_bf16(a, D, st) : launch_refine_fp8(a, D, st);
 }
-hipError_t launch_decode_scan(const DecScanArgs& a, int dtype, int D, int B, hipStream_t st) {
-  return dtype == kBF16 ? launch_decode_scan_bf16(a, D, B, st)
-                        : launch_decode_scan_fp8(a, D, B, st);
+hipError_t launch_decode_scan(const DecScanArgs& a, int dtype, int D, hipStream_t st) {
+  return dtype == kBF16 ? launch_decode_scan_bf16(a, D, st)
+                        : launch_decode_scan_fp8(a, D, st);
 }
 
 bool score_shape_supported(int dtype, int D) {
@@ -34,7 +36,7 @@ bool score_shape_supported(int dtype, int D) {
 // The binary32 sum runs over members in ascending position with no fused
 // multiply-add, then one correctly rounded division by the member count.
 // ---------------------------------------------------------------------------
-constexpr int kProxyThreads = 256;
+constexpr int kProxyThreads = 512;
 constexpr int kProxyChunk = 16;                                  // elements per 16-element chunk
 constexpr int kProxyMaxCPT = 64 * 256 / kProxyChunk / kProxyThreads;  // chunks per thread (H*D <= 16384)
 
@@ -167,8 +169,9 @@ hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st) {
 // further passes over the row in memory.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkCap = 7680;     // keys staged in LDS
-constexpr int kTopkBits1 = 12;     // first digit: bits 31..20
+constexpr int kTopkCap = kSelectCap;  // keys staged in LDS
+constexpr int kTopkBits1 = 12;        // first digit: bits 31..20
+static_assert((1 << kTopkBits1) == kSelectBins1, "first-digit histogram width");
 constexpr int kTopkU = 4;          // 16-byte loads in flight per thread
 
 __device__ inline int ref_count(const int32_t* list, int m, int t) {
@@ -302,14 +305,77 @@ __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint
   }
 }
 
+// LDS of the long-row selection.
+struct SelectShared {
+  uint32_t hist[1 << kTopkBits1];
+  uint32_t ckey[kTopkCap];
+  int32_t cslot[kTopkCap];
+  uint32_t scratch[kTopkThreads / kWave + 1];
+  uint32_t sh_bin, sh_above;
+};
+
+// Second half of a long-row selection: the first digit b1 is fixed and rem
+// keys are still needed from bin b1.  Finds the remaining 20 bits in two 10-bit
+// digits (over the ncand keys staged in LDS in index order, or, for
+// ncand < 0, over the row in memory) and emits the selection in index order.
+__device__ void select_finish(SelectShared& sm, int ncand, uint32_t b1, uint32_t rem, const float* row,
+                              int n, uint32_t m, const int32_t* list, int32_t* out) {
+  constexpr int NT = kTopkThreads;
+  const int tid = threadIdx.x;
+  uint32_t prefix = b1 << (32 - kTopkBits1);
+  uint32_t pmask = ~0u << (32 - kTopkBits1);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    for (int b = tid; b < 1024; b += NT) sm.hist[b] = 0u;
+    __syncthreads();
+    if (ncand >= 0) {
+      for (int c = tid; c < ncand; c += NT) {
+        const uint32_t key = sm.ckey[c];
+        if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 1023u], 1u);
+      }
+    } else {
+      for (int base = 0; base < n; base += kTopkU * NT * 4) {
+        float4 v[kTopkU];
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) {
+          const int s0 = base + (u * NT + tid) * 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (s0 + e >= n) continue;
+            const uint32_t key = score_key(f4(v[u], e));
+            if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 1023u], 1u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    find_bin<NT>(sm.hist, 1024, rem, sm.scratch, &sm.sh_bin, &sm.sh_above);
+    prefix |= sm.sh_bin << shift;
+    pmask |= 1023u << shift;
+    rem -= sm.sh_above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const uint32_t need_eq = rem;  // keys equal to T to take, lowest positions first
+  if (ncand >= 0) {
+    emit_selected(ncand, T, need_eq, m, list, out, sm.scratch, [&](int c, uint32_t* key, int* slot) {
+      *key = sm.ckey[c];
+      *slot = sm.cslot[c];
+    });
+  } else {
+    emit_selected(n, T, need_eq, m, list, out, sm.scratch, [&](int c, uint32_t* key, int* slot) {
+      *key = score_key(row[c]);
+      *slot = c;
+    });
+  }
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   constexpr int NT = kTopkThreads;
   constexpr int NB1 = 1 << kTopkBits1;
-  __shared__ uint32_t hist[NB1];
-  __shared__ uint32_t ckey[kTopkCap];
-  __shared__ int32_t cslot[kTopkCap];
-  __shared__ uint32_t scratch[NT / kWave + 1];
-  __shared__ uint32_t sh_bin, sh_above;
+  __shared__ SelectShared sm;
 
   const int tid = threadIdx.x;
   const int i = blockIdx.x;
@@ -327,7 +393,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
   // ---- pass 1: histogram of the top 12 bits (rows that fit are staged in LDS)
   const bool whole = n <= kTopkCap;
-  for (int b = tid; b < NB1; b += NT) hist[b] = 0u;
+  for (int b = tid; b < NB1; b += NT) sm.hist[b] = 0u;
   __syncthreads();
   for (int base = 0; base < n; base += kTopkU * NT * 4) {
     float4 v[kTopkU];
@@ -340,20 +406,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
       for (int e = 0; e < 4; ++e) {
         if (s0 + e >= n) continue;
         const uint32_t key = score_key(f4(v[u], e));
-        atomicAdd(&hist[key >> (32 - kTopkBits1)], 1u);
+        atomicAdd(&sm.hist[key >> (32 - kTopkBits1)], 1u);
         if (whole) {
-          ckey[s0 + e] = key;
-          cslot[s0 + e] = s0 + e;
+          sm.ckey[s0 + e] = key;
+          sm.cslot[s0 + e] = s0 + e;
         }
       }
     }
   }
   __syncthreads();
-  find_bin<NT>(hist, NB1, m, scratch, &sh_bin, &sh_above);
-  const uint32_t b1 = sh_bin;
-  uint32_t rem = m - sh_above;
-  const uint32_t cand_total = sh_above + hist[b1];
-  __syncthreads();  // hist is cleared below
+  find_bin<NT>(sm.hist, NB1, m, sm.scratch, &sm.sh_bin, &sm.sh_above);
+  const uint32_t b1 = sm.sh_bin;
+  const uint32_t rem = m - sm.sh_above;
+  const uint32_t cand_total = sm.sh_above + sm.hist[b1];
+  __syncthreads();  // hist is reused below
 
   int ncand;
   if (whole) {
@@ -375,12 +441,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
         if (s0 + e < n && (key[e] >> (32 - kTopkBits1)) >= b1) ++cnt;
       }
       uint32_t tot;
-      uint32_t p = running + block_exclusive_sum<NT>(cnt, scratch, &tot);
+      uint32_t p = running + block_exclusive_sum<NT>(cnt, sm.scratch, &tot);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if (s0 + e < n && (key[e] >> (32 - kTopkBits1)) >= b1) {
-          ckey[p] = key[e];
-          cslot[p] = s0 + e;
+          sm.ckey[p] = key[e];
+          sm.cslot[p] = s0 + e;
           ++p;
         }
       }
@@ -391,57 +457,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   } else {
     ncand = -1;  // fall back to passes over the row in memory
   }
-
-  uint32_t prefix = b1 << (32 - kTopkBits1);
-  uint32_t pmask = ~0u << (32 - kTopkBits1);
-  // ---- remaining 20 bits in two 10-bit digits
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    for (int b = tid; b < 1024; b += NT) hist[b] = 0u;
-    __syncthreads();
-    if (ncand >= 0) {
-      for (int c = tid; c < ncand; c += NT) {
-        const uint32_t key = ckey[c];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
-      }
-    } else {
-      for (int base = 0; base < n; base += kTopkU * NT * 4) {
-        float4 v[kTopkU];
-#pragma unroll
-        for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
-#pragma unroll
-        for (int u = 0; u < kTopkU; ++u) {
-          const int s0 = base + (u * NT + tid) * 4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (s0 + e >= n) continue;
-            const uint32_t key = score_key(f4(v[u], e));
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    find_bin<NT>(hist, 1024, rem, scratch, &sh_bin, &sh_above);
-    prefix |= sh_bin << shift;
-    pmask |= 1023u << shift;
-    rem -= sh_above;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const uint32_t need_eq = rem;  // keys equal to T to take, lowest positions first
-
-  if (ncand >= 0) {
-    emit_selected(ncand, T, need_eq, m, list, out, scratch, [&](int c, uint32_t* key, int* slot) {
-      *key = ckey[c];
-      *slot = cslot[c];
-    });
-  } else {
-    emit_selected(n, T, need_eq, m, list, out, scratch, [&](int c, uint32_t* key, int* slot) {
-      *key = score_key(row[c]);
-      *slot = c;
-    });
-  }
+  select_finish(sm, ncand, b1, rem, row, n, m, list, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -608,13 +624,183 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.nrows <= 0) return hipSuccess;
-  // rows whose length is bounded by the candidate list (Refine) fit one wave
-  const bool small = a.kind == kLenRefine && a.ldmap <= kSmallMax;
+  // rows whose length is bounded by the candidate list (Refine) fit one wave;
+  // with few rows a whole workgroup per row finishes sooner
+  const bool small = a.kind == kLenRefine && a.ldmap <= kSmallMax && a.nrows >= 1024;
   if (small)
     hipLaunchKernelGGL(topk_small_kernel, dim3((a.nrows + kSmallWaves - 1) / kSmallWaves),
                        dim3(kSmallWaves * kWave), 0, st, a);
   else
     hipLaunchKernelGGL(topk_kernel, dim3(a.nrows), dim3(kTopkThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode top-m: the decode scan has already histogrammed the top 12 key bits
+// of every row, so the threshold bin is known up front and a row can be split
+// across workgroups.  Gather: each of `parts` workgroups compacts, in index
+// order, the keys of its slice whose first digit is at or above the threshold
+// bin.  Finalize: one workgroup per row concatenates the slices in LDS (they
+// hold at most kTopkCap keys in total) and finishes the radix select; a
+// crowded threshold bin (any slice count -1) falls back to passes over the row.
+// ---------------------------------------------------------------------------
+constexpr int kGatherThreads = 256;
+
+__device__ inline int decode_row_length(const DecSelectArgs& a, int i) {
+  if (a.kind == kLenCache) {
+    const int nb = a.cache_len[i];
+    return (nb < a.g || nb > a.Lmax) ? 0 : nb;
+  }
+  const int b = i / a.g, nb = a.cache_len[b];
+  return (nb < a.g || nb > a.Lmax) ? 0 : nb - a.g + i % a.g + 1;
+}
+
+// Threshold bin of the rem-th largest key from a global 4096-bin histogram,
+// NT threads, each owning 4096/NT consecutive bins from the top.
+template <int NT>
+__device__ inline void find_bin_global(const uint32_t* hist, uint32_t rem, uint32_t* scratch, uint32_t* sh_bin,
+                                       uint32_t* sh_above) {
+  constexpr int BPT = kSelectBins1 / NT;
+  const int tid = threadIdx.x;
+  uint32_t c[BPT], sum = 0u;
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    c[e] = hist[kSelectBins1 - 1 - tid * BPT - e];
+    sum += c[e];
+  }
+  uint32_t tot;
+  uint32_t run = block_exclusive_sum<NT>(sum, scratch, &tot);
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    if (run < rem && rem <= run + c[e]) {
+      *sh_bin = (uint32_t)(kSelectBins1 - 1 - tid * BPT - e);
+      *sh_above = run;
+    }
+    run += c[e];
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kGatherThreads) void dec_gather_kernel(DecSelectArgs a) {
+  constexpr int NT = kGatherThreads;
+  constexpr int E = 16;  // elements per thread per round
+  __shared__ uint32_t scratch[NT / kWave + 1];
+  __shared__ uint32_t sh_bin, sh_above;
+  const int i = blockIdx.y, p = blockIdx.x, tid = threadIdx.x;
+  const int n = decode_row_length(a, i);
+  const uint32_t m = (uint32_t)a.m;
+  if (n <= (int)m) return;
+  const uint32_t* h = a.hist + (size_t)i * kSelectBins1;
+  find_bin_global<NT>(h, m, scratch, &sh_bin, &sh_above);
+  const uint32_t b1 = sh_bin;
+  const uint32_t cand_total = sh_above + h[b1];
+  int32_t* cnt_out = a.ccount + (size_t)i * a.parts + p;
+  if (cand_total > (uint32_t)kTopkCap) {
+    if (tid == 0) *cnt_out = -1;
+    return;
+  }
+  const int per = ((n + a.parts - 1) / a.parts + 15) / 16 * 16;
+  const int lo = p * per, hi = min(n, lo + per);
+  uint32_t* rkey = a.ckey + ((size_t)i * a.parts + p) * kTopkCap;
+  int32_t* rslot = a.cslot + ((size_t)i * a.parts + p) * kTopkCap;
+  const float* row = a.S + (long long)i * a.ldS;
+  uint32_t running = 0;
+  for (int base = lo; base < hi; base += E * NT) {
+    const int s0 = base + tid * E;
+    float4 v[E / 4];
+#pragma unroll
+    for (int u = 0; u < E / 4; ++u) v[u] = load4(row, s0 + 4 * u, hi);
+    uint32_t key[E];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      key[e] = score_key(f4(v[e >> 2], e & 3));
+      if (s0 + e < hi && (key[e] >> (32 - kTopkBits1)) >= b1) ++cnt;
+    }
+    uint32_t tot;
+    uint32_t q = running + block_exclusive_sum<NT>(cnt, scratch, &tot);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (s0 + e < hi && (key[e] >> (32 - kTopkBits1)) >= b1) {
+        rkey[q] = key[e];
+        rslot[q] = s0 + e;
+        ++q;
+      }
+    }
+    running += tot;
+  }
+  if (tid == 0) *cnt_out = (int32_t)running;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArgs a) {
+  constexpr int NT = kTopkThreads;
+  __shared__ SelectShared sm;
+  __shared__ int sh_bad;
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int n = decode_row_length(a, i);
+  const uint32_t m = (uint32_t)a.m;
+  const float* row = a.S + (long long)i * a.ldS;
+  int32_t* out = a.out + (long long)i * a.ldo;
+  if (n <= (int)m) {
+    for (int s = tid; s < (int)m; s += NT) out[s] = s < n ? s : -1;
+    return;
+  }
+  const uint32_t* h = a.hist + (size_t)i * kSelectBins1;
+  for (int b = tid; b < kSelectBins1; b += NT) sm.hist[b] = h[b];
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  find_bin<NT>(sm.hist, kSelectBins1, m, sm.scratch, &sm.sh_bin, &sm.sh_above);
+  const uint32_t b1 = sm.sh_bin;
+  const uint32_t rem = m - sm.sh_above;
+  const int32_t* cnt = a.ccount + (size_t)i * a.parts;
+  for (int q = tid; q < a.parts; q += NT)
+    if (cnt[q] < 0) sh_bad = 1;
+  __syncthreads();
+  if (sh_bad) {
+    select_finish(sm, -1, b1, rem, row, n, m, nullptr, out);
+    return;
+  }
+  // concatenate the slices in order: slice offsets first, then every entry
+  // copied in parallel (entry e belongs to the last slice starting at or before e)
+  __shared__ int sh_off[kTopkThreads + 1];
+  const int c_own = tid < a.parts ? cnt[tid] : 0;
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_sum<NT>((uint32_t)c_own, sm.scratch, &tot);
+  if (tid < a.parts) sh_off[tid] = (int)ex;
+  if (tid == 0) sh_off[a.parts] = (int)tot;
+  __syncthreads();
+  const int total = min((int)tot, kTopkCap);
+  for (int e = tid; e < total; e += NT) {
+    int lo = 0, hi = a.parts - 1;  // largest q with sh_off[q] <= e
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh_off[mid] <= e) lo = mid; else hi = mid - 1;
+    }
+    const size_t src = ((size_t)i * a.parts + lo) * kTopkCap + (e - sh_off[lo]);
+    sm.ckey[e] = a.ckey[src];
+    sm.cslot[e] = a.cslot[src];
+  }
+  __syncthreads();
+  select_finish(sm, total, b1, rem, row, n, m, nullptr, out);
+}
+
+hipError_t launch_decode_select(const DecSelectArgs& a, hipStream_t st) {
+  if (a.nrows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dec_gather_kernel, dim3(a.parts, a.nrows), dim3(kGatherThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dec_finalize_kernel, dim3(a.nrows), dim3(kTopkThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 
