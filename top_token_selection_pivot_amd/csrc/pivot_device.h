@@ -17,6 +17,7 @@ enum : int { kBF16 = 0, kFP8 = 1 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -86,16 +87,25 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // They are issued as inline assembly, outside the compiler's wait tracking, so
 // the caller waits for them explicitly (lds_dma_wait) before reading the
 // destination.  Nothing else in the kernels that use them reads M0.
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voffset) {
+//
+// The buffer descriptor of these loads: base address, no stride, `bytes` of
+// range, raw-buffer flags; every word made wave-uniform so it lives in SGPRs.
+__device__ inline i32x4 dma_rsrc(const void* base, uint32_t bytes, int flags) {
+  const uint64_t addr = (uint64_t)(uintptr_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)addr),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(addr >> 32) & 0xffff),
+               __builtin_amdgcn_readfirstlane((int)bytes), flags};
+}
+__device__ inline void lds_dma16(i32x4 rsrc, uint32_t lds, uint32_t voffset) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
                : "memory");
 }
-__device__ inline void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voffset) {
+__device__ inline void lds_dma4(i32x4 rsrc, uint32_t lds, uint32_t voffset) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
-               : "s"(lds), "v"(voffset), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
                : "memory");
 }
 // Wait until at most N vector-memory operations of the wave are outstanding

@@ -370,17 +370,17 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
 //
 // The batch's keys are cut into pairs of 32-key tiles, sequence by sequence,
 // and every workgroup takes an equal run of consecutive pairs (a run spans at
-// most a few sequences).  Inside a run each wave streams every W-th pair
-// through a ring of R stages of its own in LDS, filled by direct-to-LDS buffer
-// loads (no registers held by loads in flight): while one stage is contracted
-// the other R-1 are loading.  A stage is written in 1 KB wave-wide pieces,
+// most a few sequences).  Inside a run the waves take turns at blocks of four
+// consecutive pairs; each wave streams its pairs through a ring of R stages of
+// its own in LDS, filled by direct-to-LDS buffer loads (no registers held by
+// loads in flight): while one stage is contracted the other R-1 are loading.  A stage is written in 1 KB wave-wide pieces,
 // 16 bytes per lane, with the 16-byte chunks of each key row XOR-swizzled by
 // the row index so that the fragment reads of 32 rows spread over the banks.
 // The buffer range ends at the run's last key (reads beyond it return zero,
-// stores beyond a row's causal limit are dropped).  The scores are written,
-// and the top 12 bits of their keys are histogrammed per row in LDS and added
-// to the row's histogram in memory whenever the run moves to the next
-// sequence.
+// stores beyond a row's causal limit are dropped).  A block's 256 scores are
+// collected in LDS and written with one 16-byte-per-lane store, and the top 12
+// bits of their keys are histogrammed per row in LDS and added to the row's
+// histogram in memory whenever the run moves to the next sequence.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int QR>
 struct DecGeom {
@@ -388,7 +388,8 @@ struct DecGeom {
   static constexpr int PAIR_KEYS = 2 * kTileN;
   static constexpr int PAIR_BYTES = PAIR_KEYS * ROW;
   static constexpr int STAGE_BYTES = PAIR_BYTES + (DT == kFP8 ? PAIR_KEYS * 4 : 0);  // + key scales
-  static constexpr int FIXED = QR * kSelectBins1 * 4 + 1024;
+  static constexpr int BLOCK_PAIRS = 4;                   // pairs whose scores are stored together
+  static constexpr int FIXED = QR * kSelectBins1 * 4 + 4 * QR * BLOCK_PAIRS * PAIR_KEYS * 4 + 1024;
   static constexpr bool fits(int w, int r) { return r * w * STAGE_BYTES + FIXED <= 150 * 1024; }
   static constexpr int LOADS = PAIR_BYTES / 1024;         // wave-wide 1 KB pieces per pair
   static constexpr int STAGE_OPS = LOADS + (DT == kFP8 ? 1 : 0);  // loads that fill one stage
@@ -411,6 +412,7 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
   __shared__ __attribute__((aligned(16))) uint8_t ring1[W][G::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[R > 2 ? W : 1][R > 2 ? G::STAGE_BYTES : 16];
   __shared__ uint32_t hist[QR][NB];
+  __shared__ __attribute__((aligned(16))) float sbuf[W][QR][G::BLOCK_PAIRS * G::PAIR_KEYS];
   __shared__ uint32_t scratch[NT / kWave + 1];
   __shared__ int sh_b, sh_off;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -474,19 +476,23 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
         if constexpr (DT == kFP8) qs[i] = a.q_scale[rowi];
         pos[i] = a.qr == 1 ? nb - 1 : nb - a.g + ri;
       }
-      const int nvalid = pos[i] < 0 ? 0 : min(pos[i] + 1, k1);
+      // whole 16-byte pieces (the row stride is a multiple of 64 keys): the
+      // up-to-3 scores past the causal limit that this lets through are unused
+      const int nvalid = pos[i] < 0 ? 0 : (min(pos[i] + 1, k1) + 3) & ~3;
       srs[i] = make_rsrc(a.S + ((size_t)b * a.qr + (pos[i] < 0 ? 0 : ri)) * a.ldS, (uint32_t)nvalid * 4u);
     }
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k + ((size_t)b * a.Lmax + k0) * ROW, (uint32_t)(k1 - k0) * ROW);
-    const __amdgpu_buffer_rsrc_t ksr =
-        make_rsrc(DT == kFP8 ? a.k_scale + (size_t)b * a.Lmax + k0 : a.w, DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u);
+    const i32x4 krs = dma_rsrc(a.k + ((size_t)b * a.Lmax + k0) * ROW, (uint32_t)(k1 - k0) * ROW, kBufferFlags);
+    const i32x4 ksr = dma_rsrc(DT == kFP8 ? (const void*)(a.k_scale + (size_t)b * a.Lmax + k0) : (const void*)a.w,
+                               DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u, kBufferFlags);
 
     // the query registers are complete before the ring starts
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-    // wave-local pair s is the run's pair wid + W*s, held by stage s % R
+    // wave-local pair s is pair s % 4 of the wave's block s / 4, i.e. the
+    // segment's pair 4 * (wid + W * (s / 4)) + s % 4; stage s % R holds it
+    auto pair_of = [&](int s) { return G::BLOCK_PAIRS * (wid + W * (s / G::BLOCK_PAIRS)) + s % G::BLOCK_PAIRS; };
     auto issue = [&](const uint8_t* stage, int s) {
-      const int key0 = (wid + W * s) * G::PAIR_KEYS;
+      const int key0 = pair_of(s) * G::PAIR_KEYS;
       const uint32_t dst = lds_addr(stage);
 #pragma unroll
       for (int c = 0; c < G::LOADS; ++c) {
@@ -513,7 +519,8 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
       }
     };
     auto compute = [&](const uint8_t* stage, int s) {
-      const int key = k0 + (wid + W * s) * G::PAIR_KEYS + lane;
+      const int key = k0 + pair_of(s) * G::PAIR_KEYS + lane;
+      const int u = s % G::BLOCK_PAIRS;
       float ksv = 1.f;
       if constexpr (DT == kFP8) ksv = *reinterpret_cast<const float*>(stage + G::PAIR_BYTES + 4 * lane);
 #pragma unroll
@@ -524,13 +531,19 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
         mma_tile<DT, D, HB>(q[i], [&](int ks) { return frag_at(stage, 1, ks); }, acc1);
         float sc = pair_combine(tile_partial<DT, D, HB>(q[i], acc0), tile_partial<DT, D, HB>(q[i], acc1));
         if constexpr (DT == kFP8) sc = (sc * qs[i]) * ksv;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), srs[i], key * 4, 0, 0);
+        sbuf[wid][i][u * G::PAIR_KEYS + lane] = sc;
         if (a.hist && key < k1 && key <= pos[i]) atomicAdd(&hist[i][score_key(sc) >> 20], 1u);
+        if (u == G::BLOCK_PAIRS - 1) {
+          const int bkey = key - lane - (G::BLOCK_PAIRS - 1) * G::PAIR_KEYS;
+          const float4 v = *reinterpret_cast<const float4*>(&sbuf[wid][i][4 * lane]);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), srs[i], (bkey + 4 * lane) * 4, 0, 0);
+        }
       }
     };
 
-    // loads past the wave's last pair fall beyond the run and write zeros
-    const int npw = np > wid ? (np - wid + W - 1) / W : 0;
+    // whole blocks per wave; loads past the segment's last pair read zeros
+    const int nblk = (np + G::BLOCK_PAIRS - 1) / G::BLOCK_PAIRS;
+    const int npw = nblk > wid ? G::BLOCK_PAIRS * ((nblk - wid + W - 1) / W) : 0;
     issue(ring0[wid], 0);
     issue(ring1[wid], 1);
     if constexpr (R > 2) issue(ring2[wid], 2);
