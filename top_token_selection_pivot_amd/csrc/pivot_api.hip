@@ -432,9 +432,9 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   DecSelectArgs sel{S, p.ldS, p.rows, 0, 0, g, Lmax, cache_len, hist, p.parts,
                     (uint32_t*)(ws + p.off_ckey), (int32_t*)(ws + p.off_cslot), (int32_t*)(ws + p.off_ccount),
                     nullptr, 0};
-  PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_fill_u32(hist, (size_t)p.rows * kSelectBins1, 0u, s),
-                 "decode histogram clear");
   if (mode == PIVOT_MODE_DENSE) {
+    PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_fill_u32(hist, (size_t)p.rows * kSelectBins1, 0u, s),
+                   "decode histogram clear");
     DecScanArgs da{qb, q_scale, w, kb, k_scale, Lmax, H, cache_len, g, g, S, p.ldS, hist, B};
     PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");
     sel.m = topk;
@@ -448,7 +448,8 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   float* qbs = (float*)(ws + p.off_qs);
   float* wbar = (float*)(ws + p.off_wbar);
   int32_t* cand = cand_user ? cand_user : (int32_t*)(ws + p.off_cand);
-  ProxyArgs pa{qb, q_scale, w, B * g, H, D, g, qbar, qbs, wbar};
+  // the proxy kernel also clears the scan's histograms
+  ProxyArgs pa{qb, q_scale, w, B * g, H, D, g, qbar, qbs, wbar, hist, (size_t)p.rows * kSelectBins1};
   PIVOT_LAUNCH_K(PIVOT_K_PROXY, s, launch_proxy_mean(pa, dtype, s), "decode proxy mean");
   DecScanArgs da{qbar, qbs, wbar, kb, k_scale, Lmax, H, cache_len, g, 1, S, p.ldS, hist, B};
   PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");

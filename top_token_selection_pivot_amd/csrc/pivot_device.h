@@ -191,12 +191,15 @@ __device__ inline uint8_t f32_to_e4m3_rne_sat(float x) {
 // Wave / block scans.
 // ---------------------------------------------------------------------------
 __device__ inline uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  // Hillis-Steele within each row of 16 lanes (lanes shifted in from outside
+  // the row read 0), then the row totals are carried forward: lane 15 of
+  // rows 0 and 2 into rows 1 and 3, lane 31 (rows 0-1) into rows 2 and 3.
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 

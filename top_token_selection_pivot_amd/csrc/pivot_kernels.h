@@ -7,7 +7,8 @@
 
 namespace pivot {
 
-// Proxy mean over groups of g consecutive rows of q[R][H][D].
+// Proxy mean over groups of g consecutive rows of q[R][H][D].  Optionally
+// also clears nzero words at `zero` (a later kernel's counters).
 struct ProxyArgs {
   const uint8_t* q;
   const float* q_scale;
@@ -16,6 +17,8 @@ struct ProxyArgs {
   uint8_t* qbar;
   float* qbar_scale;
   float* wbar;
+  uint32_t* zero = nullptr;
+  size_t nzero = 0;
 };
 
 // Causal scan of query rows [row_begin, row_end) against keys k[0..Lk).

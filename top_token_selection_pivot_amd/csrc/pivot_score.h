@@ -138,21 +138,21 @@ struct KeyTile {
 // Prefill full-prefix scan.
 //
 // A workgroup = 8 waves = 8 consecutive query rows, over a chunk of kc keys.
-// Keys are staged in LDS in stages of kStageTiles tiles of 32 keys (double
-// buffered: the next stage is loaded into registers during the current one
-// and stored to LDS at its end, one barrier per stage).  Within a stage each
-// wave runs a fixed software pipeline over the tiles, with the B fragments of
-// tile t+1 read from LDS while tile t is contracted, and the epilogue of tile
-// t-1 interleaved with the contraction of tile t:
-//   tile 0: contract; finish and store the previous stage's pair (2,3)
-//   tile 1: contract; partial of tile 0
-//   tile 2: contract; partial of tile 1, store pair (0,1)
-//   tile 3: contract; partial of tile 2
+// Keys are staged in LDS in stages of ST tiles of 32 keys (double buffered:
+// the next stage is loaded into registers during the current one and stored
+// to LDS at its end, one barrier per stage).  Within a stage each wave runs a
+// fixed software pipeline over the tiles, with the B fragments of tile t+1
+// read from LDS while tile t is contracted, and the epilogue of tile t-1
+// interleaved with the contraction of tile t:
+//   even tile t: contract; finish and store the pair (t-2, t-1), which for
+//                t = 0 is the previous stage's last pair
+//   odd tile t:  contract; partial of tile t-1
 // Every tile of a stage is contracted; stores beyond a row's causal limit
 // (or the chunk end) fall outside the row's buffer range and are dropped by
 // the hardware range check, so the stage body has no data-dependent branch.
 // ---------------------------------------------------------------------------
-constexpr int kStageTiles = 4;
+constexpr int kScanStageTiles = 8;    // full-prefix scan: fewer barriers per key
+constexpr int kRefineStageTiles = 4;  // Refine: chunks of candidate slots are short
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw 32-bit buffer, range-checked
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -189,12 +189,15 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
   using Frag = typename Fmt<DT>::frag;
   constexpr int NT = ROWS * kWave;
   constexpr int NKS = D / Fmt<DT>::KSTEP;
-  constexpr int SCH = kStageTiles * KT::CHUNKS;  // 16-byte pieces per stage
+  // tiles per stage: the preferred count where two stages fit in LDS
+  constexpr int ST_PREF = GATHER ? kRefineStageTiles : kScanStageTiles;
+  constexpr int ST = 2 * ST_PREF * KT::BYTES <= 150 * 1024 ? ST_PREF : 4;
+  constexpr int SCH = ST * KT::CHUNKS;  // 16-byte pieces per stage
   constexpr int NPT = (SCH + NT - 1) / NT;
-  constexpr int STAGE_BYTES = kStageTiles * KT::BYTES;
-  constexpr int STAGE_KEYS = kStageTiles * kTileN;
+  constexpr int STAGE_BYTES = ST * KT::BYTES;
+  constexpr int STAGE_KEYS = ST * kTileN;
   constexpr int RCH = KT::ROW / 16;  // 16-byte pieces per key row
-  static_assert(kStageTiles == 4, "the pipeline below is written for 4 tiles per stage");
+  static_assert(ST % 2 == 0, "the pipeline below works on pairs of tiles");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -324,45 +327,46 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
   fetch(k0);
   stash(0);
   __syncthreads();
-  if (k0 + STAGE_KEYS < k1) fetch(k0 + STAGE_KEYS);
+  fetch(k0 + STAGE_KEYS);
 
+  // The stage body has no branch: on the first stage the "previous pair" is
+  // sent to slot -2^28 (the byte offset wraps far past every row's range),
+  // and past the chunk's last stage the prefetch reads beyond the key range
+  // (Refine: slots past the list read candidate 0); the buffer range checks
+  // drop the former and make the latter harmless.
   TileAcc<HB> acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int mb = 0; mb < HB; ++mb) acc[t].v[mb] = f32x16{};
   Frag b0[NKS], b1[NKS];
   float pa = 0.f;
   int buf = 0;
   for (int sb = k0; sb < k1; sb += STAGE_KEYS) {
     const uint8_t* st = lds + buf * STAGE_BYTES;
     load_b(st, 0, b0);
-    // tile 0
-    load_b(st, 1, b1);
-    contract(b0, acc[0]);
-    if (sb != k0) store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), sb - STAGE_KEYS + 2 * kTileN);
-    sched_tile_step();
-    // tile 1
-    load_b(st, 2, b0);
-    contract(b1, acc[1]);
-    pa = tile_partial<DT, D, HB>(qr, acc[0]);
-    sched_tile_step();
-    // tile 2
-    load_b(st, 3, b1);
-    contract(b0, acc[0]);
-    store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), sb);
-    sched_tile_step();
-    // tile 3
-    contract(b1, acc[1]);
-    pa = tile_partial<DT, D, HB>(qr, acc[0]);
-    sched_tile_step();
-
-    if (sb + STAGE_KEYS < k1) {
-      stash(buf ^ 1);
-      if (sb + 2 * STAGE_KEYS < k1) fetch(sb + 2 * STAGE_KEYS);
+#pragma unroll
+    for (int t = 0; t < ST; t += 2) {
+      // even tile: contract it, finish and store the pair before it
+      load_b(st, t + 1, b1);
+      contract(b0, acc[0]);
+      const int prev = t > 0 ? sb + (t - 2) * kTileN : sb != k0 ? sb - 2 * kTileN : -(1 << 28);
+      store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), prev);
+      sched_tile_step();
+      // odd tile: contract it, partial of the even tile
+      if (t + 2 < ST) load_b(st, t + 2, b0);
+      contract(b1, acc[1]);
+      pa = tile_partial<DT, D, HB>(qr, acc[0]);
+      sched_tile_step();
     }
+    stash(buf ^ 1);
+    fetch(sb + 2 * STAGE_KEYS);
     __syncthreads();
     buf ^= 1;
   }
-  // the last stage's pair (2,3)
+  // the last stage's last pair
   const int last = k0 + ((k1 - k0 - 1) / STAGE_KEYS) * STAGE_KEYS;
-  store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), last + 2 * kTileN);
+  store_pair(pa, tile_partial<DT, D, HB>(qr, acc[1]), last + (ST - 2) * kTileN);
 }
 
 // ---------------------------------------------------------------------------

@@ -66,6 +66,8 @@ __device__ inline void chunk_values(const ProxyArgs& a, int row, int c, float* x
 template <int DT>
 __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) {
   const int j = blockIdx.x, tid = threadIdx.x;
+  for (size_t e = (size_t)j * kProxyThreads + tid; e < a.nzero; e += (size_t)gridDim.x * kProxyThreads)
+    a.zero[e] = 0u;
   const int r0 = j * a.g;
   const int n = min(a.g, a.R - r0);
   const size_t HD = (size_t)a.H * a.D;
@@ -218,6 +220,22 @@ __device__ inline int row_length(const TopkArgs& a, int R, const int32_t** list)
   }
 }
 
+// Refine row R: its group's candidate list and the member's position t;
+// returns 0 (and no list) for a decode sequence with an invalid length.
+__device__ inline int refine_row_list(const TopkArgs& a, int R, const int32_t** list, int* t) {
+  const int j = R / a.g;
+  *list = nullptr;
+  if (a.decode) {
+    const int nb = a.cache_len[j];
+    if (nb < a.g || nb > a.Lmax) return 0;
+    *t = nb - a.g + R % a.g;
+  } else {
+    *t = R;
+  }
+  *list = a.map + (size_t)(j - a.map_grp_begin) * a.ldmap;
+  return 0;
+}
+
 // The bin (of nbins, counted from the top) that holds the rem-th largest key;
 // *above receives the number of keys in higher bins.  Thread t owns the
 // nbins/NT consecutive bins that start nbins-1-t*(nbins/NT) and go down.
@@ -262,10 +280,13 @@ __device__ inline float f4(const float4& v, int e) { return e == 0 ? v.x : e == 
 // Emits, in index order, the entries of a sequence that are selected by
 // (T, need_eq): keys above T, and the first need_eq keys equal to T.  The
 // sequence is given by get(i) -> (key, slot) for i < cnt; each thread takes
-// 4*kTopkU consecutive entries per round.
+// 4*kTopkU consecutive entries per round.  A round's selected entries fill a
+// contiguous run of the output: they are placed in LDS (`stage`, kEmitStage
+// words; any overflow is written directly) and then stored coalesced.
+constexpr int kEmitStage = kSelectBins1;
 template <typename Get>
 __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint32_t m, const int32_t* list,
-                                     int32_t* out, uint32_t* scratch, Get get) {
+                                     int32_t* out, uint32_t* scratch, int32_t* stage, Get get) {
   constexpr int E = 4 * kTopkU;
   const int tid = threadIdx.x;
   const uint32_t need_gt = m - need_eq;
@@ -285,22 +306,33 @@ __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint
     }
     uint32_t tot;
     const uint32_t excl = block_exclusive_sum<kTopkThreads>(cgt | (ceq << 16), scratch, &tot);
+    const uint32_t p0 = g_gt + min(g_eq, need_eq);  // the round's first output position
     uint32_t gt_before = g_gt + (excl & 0xFFFFu), eq_before = g_eq + (excl >> 16);
+    auto put = [&](uint32_t p, int sl) {
+      if (p >= m) return;
+      if (p - p0 < (uint32_t)kEmitStage) stage[p - p0] = sl;
+      else out[p] = list ? list[sl] : sl;
+    };
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (slot[e] < 0) continue;
       if (key[e] > T) {
-        const uint32_t p = gt_before + min(eq_before, need_eq);
-        if (p < m) out[p] = list ? list[slot[e]] : slot[e];
+        put(gt_before + min(eq_before, need_eq), slot[e]);
         ++gt_before;
       } else if (key[e] == T) {
-        const uint32_t p = gt_before + eq_before;
-        if (eq_before < need_eq && p < m) out[p] = list ? list[slot[e]] : slot[e];
+        if (eq_before < need_eq) put(gt_before + eq_before, slot[e]);
         ++eq_before;
       }
     }
     g_gt += tot & 0xFFFFu;
     g_eq += tot >> 16;
+    const uint32_t p1 = min(g_gt + min(g_eq, need_eq), m);
+    __syncthreads();
+    for (uint32_t o = tid; o < min(p1 - p0, (uint32_t)kEmitStage); o += kTopkThreads) {
+      const int sl = stage[o];
+      out[p0 + o] = list ? list[sl] : sl;
+    }
+    __syncthreads();
     if (g_gt >= need_gt && g_eq >= need_eq) break;
   }
 }
@@ -360,12 +392,14 @@ __device__ void select_finish(SelectShared& sm, int ncand, uint32_t b1, uint32_t
   const uint32_t T = prefix;
   const uint32_t need_eq = rem;  // keys equal to T to take, lowest positions first
   if (ncand >= 0) {
-    emit_selected(ncand, T, need_eq, m, list, out, sm.scratch, [&](int c, uint32_t* key, int* slot) {
+    emit_selected(ncand, T, need_eq, m, list, out, sm.scratch, reinterpret_cast<int32_t*>(sm.hist),
+                  [&](int c, uint32_t* key, int* slot) {
       *key = sm.ckey[c];
       *slot = sm.cslot[c];
     });
   } else {
-    emit_selected(n, T, need_eq, m, list, out, sm.scratch, [&](int c, uint32_t* key, int* slot) {
+    emit_selected(n, T, need_eq, m, list, out, sm.scratch, reinterpret_cast<int32_t*>(sm.hist),
+                  [&](int c, uint32_t* key, int* slot) {
       *key = score_key(row[c]);
       *slot = c;
     });
@@ -383,7 +417,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const float* row = a.S + (long long)i * a.ldS;
   int32_t* out = a.out + (long long)i * a.ldo;
   const int32_t* list;
-  const int n = row_length(a, R, &list);
+  int n;
+  if (a.kind == kLenRefine) {
+    // the entries of the ascending, -1 padded candidate list that are <= the
+    // member's position, counted in one coalesced pass
+    int t;
+    n = refine_row_list(a, R, &list, &t);
+    if (list) {
+      uint32_t c = 0;
+      for (int e = tid; e < a.ldmap; e += NT) {
+        const int v = list[e];
+        c += (v >= 0 && v <= t) ? 1u : 0u;
+      }
+      uint32_t tot;
+      block_exclusive_sum<NT>(c, sm.scratch, &tot);
+      n = (int)tot;
+    }
+  } else {
+    n = row_length(a, R, &list);
+  }
   const uint32_t m = (uint32_t)a.m;
 
   if (n <= (int)m) {
@@ -737,6 +789,13 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
   __shared__ SelectShared sm;
   __shared__ int sh_bad;
   const int i = blockIdx.x, tid = threadIdx.x;
+  // the row length, the row's histogram and the slice counts are loaded together
+  const uint32_t* h = a.hist + (size_t)i * kSelectBins1;
+  const int32_t* cnt = a.ccount + (size_t)i * a.parts;
+  uint32_t hv[kSelectBins1 / NT];
+#pragma unroll
+  for (int e = 0; e < kSelectBins1 / NT; ++e) hv[e] = h[tid + e * NT];
+  const int c_own = tid < a.parts ? cnt[tid] : 0;
   const int n = decode_row_length(a, i);
   const uint32_t m = (uint32_t)a.m;
   const float* row = a.S + (long long)i * a.ldS;
@@ -745,17 +804,14 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
     for (int s = tid; s < (int)m; s += NT) out[s] = s < n ? s : -1;
     return;
   }
-  const uint32_t* h = a.hist + (size_t)i * kSelectBins1;
-  for (int b = tid; b < kSelectBins1; b += NT) sm.hist[b] = h[b];
+#pragma unroll
+  for (int e = 0; e < kSelectBins1 / NT; ++e) sm.hist[tid + e * NT] = hv[e];
   if (tid == 0) sh_bad = 0;
   __syncthreads();
+  if (c_own < 0) sh_bad = 1;
   find_bin<NT>(sm.hist, kSelectBins1, m, sm.scratch, &sm.sh_bin, &sm.sh_above);
   const uint32_t b1 = sm.sh_bin;
   const uint32_t rem = m - sm.sh_above;
-  const int32_t* cnt = a.ccount + (size_t)i * a.parts;
-  for (int q = tid; q < a.parts; q += NT)
-    if (cnt[q] < 0) sh_bad = 1;
-  __syncthreads();
   if (sh_bad) {
     select_finish(sm, -1, b1, rem, row, n, m, nullptr, out);
     return;
@@ -763,22 +819,20 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
   // concatenate the slices in order: slice offsets first, then every entry
   // copied in parallel (entry e belongs to the last slice starting at or before e)
   __shared__ int sh_off[kTopkThreads + 1];
-  const int c_own = tid < a.parts ? cnt[tid] : 0;
   uint32_t tot;
   const uint32_t ex = block_exclusive_sum<NT>((uint32_t)c_own, sm.scratch, &tot);
   if (tid < a.parts) sh_off[tid] = (int)ex;
   if (tid == 0) sh_off[a.parts] = (int)tot;
   __syncthreads();
   const int total = min((int)tot, kTopkCap);
-  for (int e = tid; e < total; e += NT) {
-    int lo = 0, hi = a.parts - 1;  // largest q with sh_off[q] <= e
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sh_off[mid] <= e) lo = mid; else hi = mid - 1;
+  // one wave per slice (the slices hold total <= kTopkCap entries)
+  for (int q = tid >> 6; q < a.parts; q += NT / kWave) {
+    const int o = min(sh_off[q], total), c = min(sh_off[q + 1], total) - o;
+    const size_t src = ((size_t)i * a.parts + q) * kTopkCap;
+    for (int e = tid & 63; e < c; e += kWave) {
+      sm.ckey[o + e] = a.ckey[src + e];
+      sm.cslot[o + e] = a.cslot[src + e];
     }
-    const size_t src = ((size_t)i * a.parts + lo) * kTopkCap + (e - sh_off[lo]);
-    sm.ckey[e] = a.ckey[src];
-    sm.cslot[e] = a.cslot[src];
   }
   __syncthreads();
   select_finish(sm, total, b1, rem, row, n, m, nullptr, out);
