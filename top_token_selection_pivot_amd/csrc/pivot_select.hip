@@ -236,32 +236,39 @@ __device__ inline int refine_row_list(const TopkArgs& a, int R, const int32_t** 
   return 0;
 }
 
-// The bin (of nbins, counted from the top) that holds the rem-th largest key;
-// *above receives the number of keys in higher bins.  Thread t owns the
-// nbins/NT consecutive bins that start nbins-1-t*(nbins/NT) and go down.
+// The bin (of nbins, a multiple of 256, counted from the top) that holds the
+// rem-th largest key; *above receives the number of keys in higher bins.
+// One wave walks the histogram in rounds of 256 bins from the top (lane l
+// reads the four bins 4l..4l+3 below the round's top with one 16-byte read),
+// so the other waves only wait at the closing barrier.
 template <int NT>
 __device__ inline void find_bin(const uint32_t* hist, int nbins, uint32_t rem, uint32_t* scratch,
                                 uint32_t* sh_bin, uint32_t* sh_above) {
-  const int tid = threadIdx.x;
-  const int bpt = nbins / NT;  // 1 or 4
-  uint32_t c[4] = {0u, 0u, 0u, 0u}, sum = 0u;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    uint32_t above = 0;
+    for (int k = 0; k < nbins / 256; ++k) {
+      const int top = nbins - 1 - (256 * k + 4 * lane);  // the lane's highest bin
+      const uint4 v = *reinterpret_cast<const uint4*>(&hist[top - 3]);
+      const uint32_t s = v.x + v.y + v.z + v.w;
+      const uint32_t inc = wave_inclusive_sum(s);
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+      if (above + tot >= rem) {
+        uint32_t run = above + inc - s;
+        const uint32_t c[4] = {v.w, v.z, v.y, v.x};
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (e < bpt) {
-      c[e] = hist[nbins - 1 - tid * bpt - e];
-      sum += c[e];
-    }
-  uint32_t tot;
-  uint32_t run = block_exclusive_sum<NT>(sum, scratch, &tot);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (e < bpt) {
-      if (run < rem && rem <= run + c[e]) {
-        *sh_bin = (uint32_t)(nbins - 1 - tid * bpt - e);
-        *sh_above = run;
+        for (int e = 0; e < 4; ++e) {
+          if (run < rem && rem <= run + c[e]) {
+            *sh_bin = (uint32_t)(top - e);
+            *sh_above = run;
+          }
+          run += c[e];
+        }
+        break;
       }
-      run += c[e];
+      above += tot;
     }
+  }
   __syncthreads();
 }
 
@@ -284,10 +291,9 @@ __device__ inline float f4(const float4& v, int e) { return e == 0 ? v.x : e == 
 // contiguous run of the output: they are placed in LDS (`stage`, kEmitStage
 // words; any overflow is written directly) and then stored coalesced.
 constexpr int kEmitStage = kSelectBins1;
-template <typename Get>
+template <int E, typename Get>
 __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint32_t m, const int32_t* list,
                                      int32_t* out, uint32_t* scratch, int32_t* stage, Get get) {
-  constexpr int E = 4 * kTopkU;
   const int tid = threadIdx.x;
   const uint32_t need_gt = m - need_eq;
   uint32_t g_gt = 0, g_eq = 0;
@@ -295,12 +301,11 @@ __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint
     const int i0 = base + tid * E;
     uint32_t key[E];
     int slot[E];
+    get(i0, key, slot);  // entries past cnt get slot -1
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const bool valid = i0 + e < cnt;
-      if (valid) get(i0 + e, &key[e], &slot[e]);
-      else { key[e] = 0u; slot[e] = -1; }
+      const bool valid = slot[e] >= 0;
       cgt += (valid && key[e] > T) ? 1u : 0u;
       ceq += (valid && key[e] == T) ? 1u : 0u;
     }
@@ -338,7 +343,7 @@ __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint
 }
 
 // LDS of the long-row selection.
-struct SelectShared {
+struct alignas(16) SelectShared {
   uint32_t hist[1 << kTopkBits1];
   uint32_t ckey[kTopkCap];
   int32_t cslot[kTopkCap];
@@ -350,7 +355,7 @@ struct SelectShared {
 // keys are still needed from bin b1.  Finds the remaining 20 bits in two 10-bit
 // digits (over the ncand keys staged in LDS in index order, or, for
 // ncand < 0, over the row in memory) and emits the selection in index order.
-__device__ void select_finish(SelectShared& sm, int ncand, uint32_t b1, uint32_t rem, const float* row,
+__device__ __forceinline__ void select_finish(SelectShared& sm, int ncand, uint32_t b1, uint32_t rem, const float* row,
                               int n, uint32_t m, const int32_t* list, int32_t* out) {
   constexpr int NT = kTopkThreads;
   const int tid = threadIdx.x;
@@ -391,17 +396,26 @@ __device__ void select_finish(SelectShared& sm, int ncand, uint32_t b1, uint32_t
   }
   const uint32_t T = prefix;
   const uint32_t need_eq = rem;  // keys equal to T to take, lowest positions first
+  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
   if (ncand >= 0) {
-    emit_selected(ncand, T, need_eq, m, list, out, sm.scratch, reinterpret_cast<int32_t*>(sm.hist),
-                  [&](int c, uint32_t* key, int* slot) {
-      *key = sm.ckey[c];
-      *slot = sm.cslot[c];
+    // four consecutive staged entries per thread: one 16-byte read each
+    emit_selected<4>(ncand, T, need_eq, m, list, out, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(&sm.ckey[i0 < kTopkCap ? i0 : 0]);
+      const int4 sv = *reinterpret_cast<const int4*>(&sm.cslot[i0 < kTopkCap ? i0 : 0]);
+      key[0] = kv.x, key[1] = kv.y, key[2] = kv.z, key[3] = kv.w;
+      slot[0] = sv.x, slot[1] = sv.y, slot[2] = sv.z, slot[3] = sv.w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e >= ncand) slot[e] = -1;
     });
   } else {
-    emit_selected(n, T, need_eq, m, list, out, sm.scratch, reinterpret_cast<int32_t*>(sm.hist),
-                  [&](int c, uint32_t* key, int* slot) {
-      *key = score_key(row[c]);
-      *slot = c;
+    emit_selected<4 * kTopkU>(n, T, need_eq, m, list, out, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
+#pragma unroll
+      for (int e = 0; e < 4 * kTopkU; ++e) {
+        const bool valid = i0 + e < n;
+        key[e] = valid ? score_key(row[i0 + e]) : 0u;
+        slot[e] = valid ? i0 + e : -1;
+      }
     });
   }
 }
@@ -416,6 +430,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const int R = a.row_begin + i;
   const float* row = a.S + (long long)i * a.ldS;
   int32_t* out = a.out + (long long)i * a.ldo;
+  const bool whole_pre = a.kind == kLenRefine && a.ldmap <= kTopkU * NT * 4;
+  for (int b = tid; b < NB1; b += NT) sm.hist[b] = 0u;
+  // a Refine row has at most ldmap scores: when they fit one pass-1 round
+  // they are loaded while the row length is still being counted
+  float4 v[kTopkU];
+  if (whole_pre) {
+#pragma unroll
+    for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, (u * NT + tid) * 4, a.ldmap);
+  }
   const int32_t* list;
   int n;
   if (a.kind == kLenRefine) {
@@ -445,12 +468,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
   // ---- pass 1: histogram of the top 12 bits (rows that fit are staged in LDS)
   const bool whole = n <= kTopkCap;
-  for (int b = tid; b < NB1; b += NT) sm.hist[b] = 0u;
   __syncthreads();
   for (int base = 0; base < n; base += kTopkU * NT * 4) {
-    float4 v[kTopkU];
+    if (!(whole_pre && base == 0)) {
 #pragma unroll
-    for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
+      for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
+    }
 #pragma unroll
     for (int u = 0; u < kTopkU; ++u) {
       const int s0 = base + (u * NT + tid) * 4;
@@ -825,13 +848,31 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
   if (tid == 0) sh_off[a.parts] = (int)tot;
   __syncthreads();
   const int total = min((int)tot, kTopkCap);
-  // one wave per slice (the slices hold total <= kTopkCap entries)
-  for (int q = tid >> 6; q < a.parts; q += NT / kWave) {
-    const int o = min(sh_off[q], total), c = min(sh_off[q + 1], total) - o;
-    const size_t src = ((size_t)i * a.parts + q) * kTopkCap;
-    for (int e = tid & 63; e < c; e += kWave) {
-      sm.ckey[o + e] = a.ckey[src + e];
-      sm.cslot[o + e] = a.cslot[src + e];
+  // entry e (of total <= kTopkCap) comes from the last slice starting at or
+  // before e; every load of a thread is issued before its entries are stored
+  constexpr int PER = (kTopkCap + NT - 1) / NT;
+  uint32_t kk[PER];
+  int32_t ss[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + u * NT;
+    if (e < total) {
+      int lo = 0, hi = a.parts - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh_off[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      const size_t src = ((size_t)i * a.parts + lo) * kTopkCap + (e - sh_off[lo]);
+      kk[u] = a.ckey[src];
+      ss[u] = a.cslot[src];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + u * NT;
+    if (e < total) {
+      sm.ckey[e] = kk[u];
+      sm.cslot[e] = ss[u];
     }
   }
   __syncthreads();
