@@ -51,6 +51,8 @@ def parse():
                     help="budget of the CPU-oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run 3 plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the MTP decode step (used under a profiler)")
     return ap.parse_args()
 
 
@@ -79,6 +81,92 @@ def time_steps(fn, steps, warmup, torch):
         fn()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+def measure_decode(torch, pv, synth, nd_steps, nd_prof):
+    """The MTP decode step (B=32, g=2, fp8 cache of 32K-128K keys, Refine):
+    microseconds per step without per-kernel events, then a profiled pass for
+    the per-kernel times and the decode scan's HBM rate."""
+    topk, C, H, D = 2048, 4096, 64, 128
+    log("generating the decode inputs")
+    dec = synth.make("decode_mtp_b32")
+    dd = upload(dec, torch)
+    B, Lmax = dec.B, dec.Lmax
+    dws = torch.empty(max(pv.decode_workspace_size(B, Lmax, H, D, 2, topk, C, m, 1)
+                          for m in ("refine", "dense")), dtype=torch.uint8, device="cuda")
+    dout = torch.empty((B, 2, topk), dtype=torch.int32, device="cuda")
+
+    def dstep(mode="refine"):
+        pv.indexer_decode(dd["q"], dd["w"], dd["k"], dd["cache_len"], topk=topk, C=C,
+                          mode=mode, q_scale=dd["q_scale"], k_scale=dd["k_scale"], out=dout,
+                          workspace=dws)
+
+    for _ in range(10):
+        dstep()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(nd_steps):
+        dstep()
+    torch.cuda.synchronize()
+    dsec = (time.perf_counter() - t0) / nd_steps
+    pv.profile_enable(True)
+    pv.profile_read()
+    for _ in range(nd_prof):
+        dstep()
+    torch.cuda.synchronize()
+    dprof = pv.profile_read()
+    pv.profile_enable(False)
+    key_bytes = float(dec.cache_len.astype(np.int64).sum()) * (D + 4)
+    scan_ms_d = dprof["decode_scan"][0] / nd_prof
+    dense_dsec = time_steps(lambda: dstep("dense"), max(1, nd_steps // 2), 5, torch)
+    res = {
+        "workload": "decode_mtp_b32 (B=32, g=2, fp8, cache 32K-128K)",
+        "us_per_step": dsec * 1e6,
+        "dense_us_per_step": dense_dsec * 1e6,
+        "key_stream_bytes": key_bytes,
+        "decode_scan_us": scan_ms_d * 1e3,
+        "decode_scan_hbm_GBs": key_bytes / (scan_ms_d / 1e3) / 1e9,
+        "decode_scan_hbm_frac": key_bytes / (scan_ms_d / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "kernels_us": {k: v[0] / nd_prof * 1e3 for k, v in dprof.items() if v[1]},
+    }
+    log(f"decode {dsec*1e6:.1f} us/step; scan {key_bytes/(scan_ms_d/1e3)/1e9:.0f} GB/s")
+    del dd, dws, dout
+    torch.cuda.empty_cache()
+    return res
+
+
+# Sources of the full-prefix scan kernel: the HBM bytes measured with
+# rocprofv3 counters (FETCH_SIZE, WRITE_SIZE, calibrated on a plain copy) are
+# reported only while these files are unchanged since the measurement.
+SCAN_SOURCES = ("pivot_device.h", "pivot_kernels.h", "pivot_score.h", "pivot_score_launch.h",
+                "score_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_128k_refine_g8_hbm_counters.md")
+
+
+def scan_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        with open(os.path.join(ROOT, "top_token_selection_pivot_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per scan launch from the committed counter summary, or None
+    when it is missing or the scan's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("scan-traffic:"):
+                    f = dict(kv.split("=") for kv in line.split(":", 1)[1].split())
+                    if f.get("sources") == scan_source_hash():
+                        return {"fetch_bytes": float(f["fetch"]), "write_bytes": float(f["write"]),
+                                "bytes": float(f["fetch"]) + float(f["write"]),
+                                "per": "launch", "source": os.path.basename(TRAFFIC_FILE)}
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
 
 
 def proxy_scan_pairs(L, g):
@@ -139,6 +227,13 @@ def main():
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
+    if args.decode_only:
+        res = measure_decode(torch, pv, synth, args.steps, args.steps)
+        print(json.dumps({"metric": "decode us/step (MTP, B=32, g=2, fp8, Refine)",
+                          "value": res["us_per_step"], "unit": "us/step", "n_gpus": 1,
+                          "steps": args.steps, "higher_is_better": False, "decode": res}),
+              flush=True)
+        return
     L, H, D, g, topk, C = 131072, 64, 128, args.g, 2048, 4096
     log("generating the 128K prefill inputs")
     inp = synth.make("prefill_128k")
@@ -195,7 +290,7 @@ def main():
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / BF16_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": committed_traffic(),
             "launches_per_step": scan_n / args.steps,
             "avg_launch_ms": scan_ms / max(1, scan_n),
             "algorithmic_flops_per_step": 2.0 * H * D * proxy_scan_pairs(L, g),
@@ -255,58 +350,11 @@ def main():
         del d, ws, out
         torch.cuda.empty_cache()
 
-        # decode: one MTP step, B=32 sequences, fp8 key cache
-        log("generating the decode inputs")
-        dec = synth.make("decode_mtp_b32")
-        dd = upload(dec, torch)
-        B, Lmax = dec.B, dec.Lmax
-        dws = torch.empty(max(pv.decode_workspace_size(B, Lmax, H, D, 2, topk, C, m, 1)
-                              for m in ("refine", "dense")), dtype=torch.uint8, device="cuda")
-        dout = torch.empty((B, 2, topk), dtype=torch.int32, device="cuda")
-
-        def dstep(mode="refine"):
-            pv.indexer_decode(dd["q"], dd["w"], dd["k"], dd["cache_len"], topk=topk, C=C,
-                              mode=mode, q_scale=dd["q_scale"], k_scale=dd["k_scale"], out=dout,
-                              workspace=dws)
-
-        for _ in range(10):
-            dstep()
-        torch.cuda.synchronize()
-        # the step time without per-kernel events, then a profiled pass for the breakdown
-        nd_steps = 200
-        t0 = time.perf_counter()
-        for _ in range(nd_steps):
-            dstep()
-        torch.cuda.synchronize()
-        dsec = (time.perf_counter() - t0) / nd_steps
-        pv.profile_enable(True)
-        pv.profile_read()
-        nd_prof = 100
-        for _ in range(nd_prof):
-            dstep()
-        torch.cuda.synchronize()
-        dprof = pv.profile_read()
-        pv.profile_enable(False)
-        key_bytes = float(dec.cache_len.astype(np.int64).sum()) * (D + 4)
-        scan_ms_d = dprof["decode_scan"][0] / nd_prof
-        dense_dsec = time_steps(lambda: dstep("dense"), 100, 5, torch)
-        extras["decode"] = {
-            "workload": "decode_mtp_b32 (B=32, g=2, fp8, cache 32K-128K)",
-            "us_per_step": dsec * 1e6,
-            "dense_us_per_step": dense_dsec * 1e6,
-            "key_stream_bytes": key_bytes,
-            "decode_scan_us": scan_ms_d * 1e3,
-            "decode_scan_hbm_GBs": key_bytes / (scan_ms_d / 1e3) / 1e9,
-            "decode_scan_hbm_frac": key_bytes / (scan_ms_d / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "kernels_us": {k: v[0] / nd_prof * 1e3 for k, v in dprof.items() if v[1]},
-        }
-        log(f"decode {dsec*1e6:.1f} us/step; scan {key_bytes/(scan_ms_d/1e3)/1e9:.0f} GB/s")
+        extras["decode"] = measure_decode(torch, pv, synth, 200, 100)
         extras["pages_claims_context"] = ("up to 4x indexer speedup, about 3x for Refine, "
                                           "1.6x end-to-end on DeepSeek-V3.2/GLM-5.1; "
                                           "no hardware stated")
         result["extras"] = extras
-        del dd, dws, dout
-        torch.cuda.empty_cache()
 
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         cqps, cdt, groups = cpu_baseline(inp, g, topk, C, args.cpu_seconds)
