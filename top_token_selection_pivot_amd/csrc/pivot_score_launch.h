@@ -6,6 +6,15 @@
 
 namespace pivot {
 
+// Compute units of the current device.
+static inline int device_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus < 1)
+    cus = 1;
+  return cus;
+}
+
 template <int DT, int D, int HB>
 static void scan_one(const ScanArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((score_block_kernel<DT, D, HB, false, kScanRows, ScanArgs>), grid, dim3(kScanRows * kWave), 0,
@@ -33,11 +42,7 @@ static void decode_launch(const DecScanArgs& a, int zblocks, hipStream_t st) {
       nblk = 1;
     return nblk;
   }();
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                              hipSuccess || cus < 1)
-    cus = 1;
-  dim3 grid(cus * per_cu, 1, zblocks);
+  dim3 grid(device_cu_count() * per_cu, 1, zblocks);
   hipLaunchKernelGGL((decode_scan_kernel<DT, D, HB, QR>), grid, dim3(G::THREADS), 0, st, a);
 }
 template <int DT, int D, int HB>
@@ -69,8 +74,27 @@ static bool dispatch_shape(int D, int H, F&& f) {
   return false;
 }
 
+constexpr int kScanMaxKeyChunk = 16384;
+
+// Keys per scan workgroup: a.kc at least, and as long as keeps about 8
+// workgroups per compute unit over this launch's causal triangle (each
+// workgroup first loads its 8 query rows and first key stage, so longer
+// chunks amortise that), at most kScanMaxKeyChunk.
+static inline int scan_key_chunk(const ScanArgs& a) {
+  long long total = 0;
+  for (int rb = a.row_begin; rb < a.row_end; rb += kScanRows) {
+    const int rl = min(rb + kScanRows, a.row_end) - 1;
+    total += min(rl * a.pos_mul + a.pos_add, a.pos_cap) + 1;
+  }
+  long long kc = total / (8LL * device_cu_count());
+  kc = (kc + 255) / 256 * 256;
+  return (int)std::max<long long>(a.kc, std::min<long long>(kc, kScanMaxKeyChunk));
+}
+
 template <int DT>
-hipError_t launch_scan_dt(const ScanArgs& a, int D, hipStream_t st) {
+hipError_t launch_scan_dt(const ScanArgs& a_in, int D, hipStream_t st) {
+  ScanArgs a = a_in;
+  a.kc = scan_key_chunk(a_in);
   const int nrows = a.row_end - a.row_begin;
   const int rlast = a.row_end - 1;
   const int lim = min(rlast * a.pos_mul + a.pos_add, a.pos_cap) + 1;
