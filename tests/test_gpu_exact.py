@@ -198,6 +198,23 @@ def test_chunked_passes_match_single_pass():
         assert np.array_equal(big, small), mode
 
 
+def test_long_exact_sampled_groups():
+    # L = 32768, H = 64, D = 128 on small integers: the scan runs several key
+    # chunks per workgroup row block (longer than the shortest chunk), so chunk
+    # edges are checked bit-exactly; whole groups are sampled across the range
+    print("case: L=32768 H=64 D=128 integer inputs, Refine g=8, sampled groups", flush=True)
+    L, g, topk, C = 32768, 8, 256, 512
+    inp = synth.small_integer(L, 64, 128, seed=31, qmax=2, kmax=2, wmax=3)
+    out = _run(inp, "refine", g, topk, C)
+    v = oracle.View.of(inp)
+    G = L // g
+    rng = np.random.default_rng(5)
+    groups = sorted(set([0, 1, G // 2, G - 2, G - 1]) | set(rng.integers(0, G, 10).tolist()))
+    for j in groups:
+        ref, _, _ = oracle.group(v, j * g, j * g, g, topk, C, "refine")
+        assert np.array_equal(out[j * g:(j + 1) * g], ref), j
+
+
 def test_deterministic_repeat():
     print("case: repeated calls are identical", flush=True)
     inp = synth.dsa_prefill(L=4096, H=64, D=128, seed=12)

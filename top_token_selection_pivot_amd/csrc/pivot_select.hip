@@ -548,8 +548,19 @@ constexpr int kSmallChunks = kSmallMax / 256;
 
 __device__ inline uint32_t wave_exclusive_sum(uint32_t v, uint32_t* total) {
   const uint32_t inc = wave_inclusive_sum(v);
-  *total = __shfl(inc, 63, 64);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
   return inc - v;
+}
+
+// Maximum over the wave (DPP row shifts and row broadcasts, then lane 63).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));   // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));   // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));   // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));   // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
 // Orders this wave's LDS accesses across lanes (wave-scope fence + barrier).
@@ -568,37 +579,46 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
   const int R = a.row_begin + i;
   const float* row = a.S + (long long)i * a.ldS;
   int32_t* out = a.out + (long long)i * a.ldo;
-  const int32_t* list;
-  const int n = row_length(a, R, &list);
   const uint32_t m = (uint32_t)a.m;
-  if (n <= (int)m) {
-    for (int s = lane; s < (int)m; s += kWave) out[s] = s < n ? (list ? list[s] : s) : -1;
+  // the row (at most ldmap <= kSmallMax scores) and its candidate positions
+  // are loaded up front; the row length, the number of candidates <= the
+  // member's position (a prefix of the ascending list), is counted from them
+  const int32_t* list;
+  int t;
+  refine_row_list(a, R, &list, &t);
+  if (!list) {
+    for (int s = lane; s < (int)m; s += kWave) out[s] = -1;
     return;
   }
-
-  // keys and output values (candidate positions, or the slots themselves) of
-  // this lane's elements, all loaded up front
+  const int lmax = a.ldmap;
   uint32_t key[kSmallChunks * 4];
   int32_t val[kSmallChunks * 4];
-  const bool list16 = list && ((uintptr_t)list & 15u) == 0;  // 16-byte loads of the list
+  const bool list16 = ((uintptr_t)list & 15u) == 0;  // 16-byte loads of the list
+  uint32_t cnt_le = 0;
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c) {
     const int s0 = c * 256 + lane * 4;
-    const float4 v = load4(row, s0, n);
-    i32x4 p = i32x4{s0, s0 + 1, s0 + 2, s0 + 3};
-    if (list) {
-      if (list16 && s0 + 3 < n) {
-        p = *reinterpret_cast<const i32x4*>(list + s0);
-      } else {
+    const float4 v = load4(row, s0, lmax);
+    i32x4 p;
+    if (list16 && s0 + 3 < lmax) {
+      p = *reinterpret_cast<const i32x4*>(list + s0);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = s0 + e < n ? list[s0 + e] : -1;
-      }
+      for (int e = 0; e < 4; ++e) p[e] = s0 + e < lmax ? list[s0 + e] : -1;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       key[c * 4 + e] = score_key(f4(v, e));
       val[c * 4 + e] = p[e];
+      cnt_le += (p[e] >= 0 && p[e] <= t) ? 1u : 0u;
     }
+  }
+  uint32_t n_u;
+  wave_exclusive_sum(cnt_le, &n_u);
+  const int n = (int)n_u;
+  if (n <= (int)m) {
+    for (int s = lane; s < (int)m; s += kWave) out[s] = s < n ? list[s] : -1;
+    return;
   }
   auto valid = [&](int c, int e) { return c * 256 + lane * 4 + e < n; };
 
@@ -612,11 +632,8 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
         kmin = min(kmin, key[c * 4 + e]);
         kmax = max(kmax, key[c * 4 + e]);
       }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
-  }
+  kmax = wave_max_u32(kmax);
+  kmin = ~wave_max_u32(~kmin);
   int top = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));  // undetermined low bits
   uint32_t pmask = top == 32 ? 0u : ~0u << top;
   uint32_t prefix = kmax & pmask, rem = m;
@@ -655,8 +672,8 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
     }
     const unsigned long long hit = __ballot(found >= 0);
     const int src = hit ? __ffsll((long long)hit) - 1 : 0;
-    const uint32_t digit = (uint32_t)__shfl(found, src, 64);
-    above = __shfl(above, src, 64);
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(found, src);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)above, src);
     prefix |= digit << shift;
     pmask |= dmask << shift;
     rem -= above;
