@@ -30,6 +30,7 @@
 namespace pivot {
 
 constexpr int kScanRows = 8;      // query rows (waves) per scoring workgroup
+constexpr int kRefineSlotMax = 4096;  // candidate slots per Refine workgroup
 constexpr int kLdsPad = 16;       // bytes of padding per staged key row
 
 // Per-wave query state: A fragments of every head block and contraction step,
@@ -199,6 +200,7 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
   constexpr int RCH = KT::ROW / 16;  // 16-byte pieces per key row
   static_assert(ST % 2 == 0, "the pipeline below works on pairs of tiles");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE_BYTES];
+  __shared__ int32_t cand_s[GATHER ? kRefineSlotMax : 1];  // Refine: positions of slots [k0, k1)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -274,9 +276,15 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
     }
   }
 
-  // key position of slot `slot` (Refine) -- 0 past the candidate list
+  // key position of slot `slot` (Refine) -- 0 outside the workgroup's slots
+  if constexpr (GATHER) {
+    for (int e = tid; e < k1 - k0; e += NT) cand_s[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, e * 4, 0, 0);
+    __syncthreads();
+  }
   auto cand_pos = [&](int slot) -> int {
-    return (int)__builtin_amdgcn_raw_buffer_load_b32(crs, (slot - k0) * 4, 0, 0);
+    const int r = slot - k0;
+    const int v = cand_s[(unsigned)r < (unsigned)(k1 - k0) ? r : 0];
+    return (unsigned)r < (unsigned)(k1 - k0) ? v : 0;
   };
 
   i32x4 pre[NPT];

@@ -112,7 +112,7 @@ hipError_t launch_refine_dt(const RefineArgs& a_in, int D, hipStream_t st) {
   const int zblocks = (a.g + rows - 1) / rows;
   // all candidates in one workgroup when there are enough groups to fill the
   // chip (each member's query is then loaded once); 256-slot pieces otherwise
-  a.slot_chunk = (long long)ngrp * zblocks >= 2048 ? a.m : 256;
+  a.slot_chunk = (long long)ngrp * zblocks >= 2048 ? min(a.m, kRefineSlotMax) : 256;
   dim3 grid((a.m + a.slot_chunk - 1) / a.slot_chunk, ngrp, zblocks);
   auto f = [&]<int D_, int HB_>() { refine_one<DT, D_, HB_>(a, grid, rows, st); };
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
