@@ -268,6 +268,26 @@ def test_decode_exact_many_sequences(dtype, mode):
         assert np.array_equal(out[b], ref), b
 
 
+@pytest.mark.parametrize("mode", ["dense", "refine"])
+def test_decode_exact_many_short_sequences(mode):
+    # B = 300 > 256: the decode scan's division of the batch into per-workgroup
+    # runs counts sequences in several blocks; short and invalid lengths mixed
+    print(f"case: decode exact B=300 H=8 D=64 bf16 {mode}", flush=True)
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(2, 700, 300)]
+    lens[0], lens[17], lens[255], lens[256], lens[299] = 1, 0, 700, 64, 2
+    dec = _decode_inputs(300, lens, g=2, H=8, D=64, Lmax=700, seed=42)
+    d = to_device(dec)
+    out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=32, C=96,
+                            mode=mode).cpu().numpy()
+    for b in range(300):
+        if lens[b] < 2:
+            assert np.all(out[b] == -1), b
+            continue
+        ref, _, _ = oracle.decode_seq(dec, b, 32, 96, mode)
+        assert np.array_equal(out[b], ref), b
+
+
 def test_decode_matches_last_prefill_group_and_rejects_bad_lengths():
     print("case: decode == last prefill group; invalid cache lengths give -1 rows", flush=True)
     g = 4
