@@ -537,14 +537,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Top-m of short rows (n <= 4096, e.g. a member's candidates): one wave per
-// row.  The row's keys live in registers (64 per lane), the radix select runs
-// four 8-bit digits against a private 256-bin LDS histogram per wave, and the
-// index-ordered emission is a wave-level scan, so no workgroup barrier is
-// needed.  Lane l holds elements 256*i + 4*l .. 256*i + 4*l + 3 of chunk i.
+// row.  The row's keys live in registers (64 per lane) and the radix select
+// runs 8-bit digits against a private 256-bin LDS histogram per wave, starting
+// below the bits all of the row's keys share.  After the first digit the keys
+// of the threshold bin (usually a few percent of the row) are compacted into
+// LDS and the remaining digits run on that short list.  The index-ordered
+// emission is a wave-level scan, so no workgroup barrier is needed.  Lane l
+// holds elements 256*i + 4*l .. 256*i + 4*l + 3 of chunk i.
 // ---------------------------------------------------------------------------
 constexpr int kSmallMax = 4096;
 constexpr int kSmallWaves = 4;
 constexpr int kSmallChunks = kSmallMax / 256;
+constexpr int kSmallCand = 512;  // threshold-bin keys a wave compacts for its later digits
 
 __device__ inline uint32_t wave_exclusive_sum(uint32_t v, uint32_t* total) {
   const uint32_t inc = wave_inclusive_sum(v);
@@ -571,11 +575,13 @@ __device__ inline void wave_sync() {
 
 __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArgs a) {
   __shared__ uint32_t hist_all[kSmallWaves][256];
+  __shared__ uint32_t cand_all[kSmallWaves][kSmallCand];
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int i = blockIdx.x * kSmallWaves + wid;
   if (i >= a.nrows) return;
   uint32_t* hist = hist_all[wid];
+  uint32_t* cand = cand_all[wid];
   const int R = a.row_begin + i;
   const float* row = a.S + (long long)i * a.ldS;
   int32_t* out = a.out + (long long)i * a.ldo;
@@ -620,36 +626,38 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
     for (int s = lane; s < (int)m; s += kWave) out[s] = s < n ? list[s] : -1;
     return;
   }
-  auto valid = [&](int c, int e) { return c * 256 + lane * 4 + e < n; };
-
-  // bits above the highest bit where the row's keys differ are common to all
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  // Entries past the row get key 0.  No score has key 0 (it would be a NaN),
+  // so they rank below every entry of the row: they never reach the threshold
+  // and are never emitted.
+  uint32_t kmax = 0u, kmin1 = 0xFFFFFFFFu;  // kmin1: smallest key - 1 of the row
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (valid(c, e)) {
-        kmin = min(kmin, key[c * 4 + e]);
-        kmax = max(kmax, key[c * 4 + e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = c * 256 + lane * 4 + e < n ? key[c * 4 + e] : 0u;
+      key[c * 4 + e] = k;
+      kmax = max(kmax, k);
+      kmin1 = min(kmin1, k - 1u);
+    }
   kmax = wave_max_u32(kmax);
-  kmin = ~wave_max_u32(~kmin);
+  const uint32_t kmin = ~wave_max_u32(~kmin1) + 1u;
+  // bits above the highest bit where the row's keys differ are common to all
   int top = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));  // undetermined low bits
   uint32_t pmask = top == 32 ? 0u : ~0u << top;
   uint32_t prefix = kmax & pmask, rem = m;
-  while (top > 0) {
+
+  // One 8-bit (or narrower) digit below the fixed prefix over the keys that
+  // visit(f) hands to f; returns how many of them fall in the chosen bin.
+  auto digit_pass = [&](auto visit) -> uint32_t {
     const int width = top < 8 ? top : 8;
     const int shift = top - width;
     const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
     for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0u;
     wave_sync();
-#pragma unroll
-    for (int c = 0; c < kSmallChunks; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (valid(c, e) && (key[c * 4 + e] & pmask) == prefix)
-          atomicAdd(&hist[(key[c * 4 + e] >> shift) & dmask], 1u);
+    visit([&](uint32_t k) {
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+    });
     wave_sync();
     // lane l owns bins 255-4l .. 252-4l (descending)
     uint32_t cnt[4], sum = 0;
@@ -661,12 +669,13 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
     uint32_t tot;
     uint32_t run = wave_exclusive_sum(sum, &tot);
     int found = -1;
-    uint32_t above = 0;
+    uint32_t above = 0, inbin = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       if (found < 0 && run < rem && rem <= run + cnt[b]) {
         found = 255 - lane * 4 - b;
         above = run;
+        inbin = cnt[b];
       }
       run += cnt[b];
     }
@@ -674,30 +683,61 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
     const int src = hit ? __ffsll((long long)hit) - 1 : 0;
     const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(found, src);
     above = (uint32_t)__builtin_amdgcn_readlane((int)above, src);
+    inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, src);
     prefix |= digit << shift;
     pmask |= dmask << shift;
     rem -= above;
     top = shift;
     wave_sync();
-  }
-  const uint32_t T = prefix, need_eq = rem, need_gt = m - rem;
+    return inbin;
+  };
+  auto visit_row = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < kSmallChunks * 4; ++j) f(key[j]);
+  };
 
+  uint32_t inbin = top > 0 ? digit_pass(visit_row) : 0u;
+  if (top > 0 && inbin <= (uint32_t)kSmallCand) {
+    // compact the threshold bin's keys (any order: only their values matter)
+    uint32_t base = 0;
+#pragma unroll
+    for (int j = 0; j < kSmallChunks * 4; ++j) {
+      const bool hit = (key[j] & pmask) == prefix;
+      const unsigned long long mk = __ballot(hit);
+      if (hit) cand[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = key[j];
+      base += (uint32_t)__popcll(mk);
+    }
+    wave_sync();
+    uint32_t ck[kSmallCand / kWave];
+#pragma unroll
+    for (int j = 0; j < kSmallCand / kWave; ++j) ck[j] = cand[j * kWave + lane];
+    const uint32_t nc = inbin;
+    auto visit_cand = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < kSmallCand / kWave; ++j)
+        if ((uint32_t)(j * kWave + lane) < nc) f(ck[j]);
+    };
+    while (top > 0) digit_pass(visit_cand);
+  } else {
+    while (top > 0) digit_pass(visit_row);
+  }
+  const uint32_t T = prefix, need_eq = rem;
+
+  // emission in index order (entries past the row hold key 0 < T)
   uint32_t g_gt = 0, g_eq = 0;
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c) {
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool v = valid(c, e);
-      cgt += (v && key[c * 4 + e] > T) ? 1u : 0u;
-      ceq += (v && key[c * 4 + e] == T) ? 1u : 0u;
+      cgt += key[c * 4 + e] > T ? 1u : 0u;
+      ceq += key[c * 4 + e] == T ? 1u : 0u;
     }
     uint32_t tot;
     const uint32_t excl = wave_exclusive_sum(cgt | (ceq << 16), &tot);
     uint32_t gt_before = g_gt + (excl & 0xFFFFu), eq_before = g_eq + (excl >> 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (!valid(c, e)) continue;
       const uint32_t kk = key[c * 4 + e];
       if (kk > T) {
         const uint32_t p = gt_before + min(eq_before, need_eq);
