@@ -288,6 +288,25 @@ def test_decode_exact_many_short_sequences(mode):
         assert np.array_equal(out[b], ref), b
 
 
+@pytest.mark.parametrize("dtype,D", [("fp8", 64), ("fp8", 256), ("bf16", 32), ("bf16", 256)])
+@pytest.mark.parametrize("mode", ["dense", "refine"])
+def test_decode_exact_head_dims(dtype, D, mode):
+    # every key width has its own decode-scan geometry (waves per workgroup,
+    # ring depth); sequences end inside and across the workgroups' runs
+    print(f"case: decode exact B=12 H=16 D={D} {dtype} {mode}", flush=True)
+    rng = np.random.default_rng(D + (dtype == "fp8"))
+    lens = [int(x) for x in rng.integers(2, 3000, 12)]
+    lens[1], lens[5], lens[6] = 3000, 64, 2
+    dec = _decode_inputs(12, lens, g=2, H=16, D=D, dtype=dtype, Lmax=3000, seed=D)
+    d = to_device(dec)
+    kw = dict(q_scale=d["q_scale"], k_scale=d["k_scale"]) if dtype == "fp8" else {}
+    out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=48, C=160, mode=mode,
+                            **kw).cpu().numpy()
+    for b in range(12):
+        ref, _, _ = oracle.decode_seq(dec, b, 48, 160, mode)
+        assert np.array_equal(out[b], ref), b
+
+
 def test_decode_matches_last_prefill_group_and_rejects_bad_lengths():
     print("case: decode == last prefill group; invalid cache lengths give -1 rows", flush=True)
     g = 4

@@ -401,11 +401,14 @@ struct DecGeom {
   static constexpr int PAIR_BYTES = PAIR_KEYS * ROW;
   static constexpr int STAGE_BYTES = PAIR_BYTES + (DT == kFP8 ? PAIR_KEYS * 4 : 0);  // + key scales
   static constexpr int BLOCK_PAIRS = 4;                   // pairs whose scores are stored together
-  static constexpr int FIXED = QR * kSelectBins1 * 4 + 4 * QR * BLOCK_PAIRS * PAIR_KEYS * 4 + 1024;
-  static constexpr bool fits(int w, int r) { return r * w * STAGE_BYTES + FIXED <= 150 * 1024; }
+  static constexpr int FIXED_W = QR * BLOCK_PAIRS * PAIR_KEYS * 4;  // per-wave score block
+  static constexpr bool fits(int w, int r) {
+    return r * w * STAGE_BYTES + w * FIXED_W + QR * kSelectBins1 * 4 + 1024 <= 158 * 1024;
+  }
   static constexpr int LOADS = PAIR_BYTES / 1024;         // wave-wide 1 KB pieces per pair
   static constexpr int STAGE_OPS = LOADS + (DT == kFP8 ? 1 : 0);  // loads that fill one stage
-  static constexpr int W = (fits(4, 3) || fits(4, 2)) ? 4 : (fits(2, 3) || fits(2, 2)) ? 2 : 1;
+  // two waves per SIMD when their rings fit (their compute overlaps), else one
+  static constexpr int W = fits(8, 2) ? 8 : (fits(4, 3) || fits(4, 2)) ? 4 : (fits(2, 3) || fits(2, 2)) ? 2 : 1;
   // a wait names the newer stages' loads in a 6-bit count
   static constexpr int R = (fits(W, 3) && 2 * STAGE_OPS < 64) ? 3 : 2;
   static constexpr int THREADS = W * kWave;

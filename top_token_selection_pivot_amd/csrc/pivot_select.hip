@@ -39,27 +39,44 @@ bool score_shape_supported(int dtype, int D) {
 constexpr int kProxyThreads = 512;
 constexpr int kProxyChunk = 16;                                  // elements per 16-element chunk
 constexpr int kProxyMaxCPT = 64 * 256 / kProxyChunk / kProxyThreads;  // chunks per thread (H*D <= 16384)
+constexpr int kProxyU = 4;  // members whose loads are issued together
 
-// The 16 values of chunk c of row `row` (binary32; fp8 codes times the row scale).
+// Chunk c of row `row` as loaded (16 codes; the row scale for fp8) ...
+struct ChunkRaw {
+  i32x4 lo, hi;  // bf16: 8 + 8 codes; fp8: lo holds all 16 codes
+  float s;
+};
 template <int DT>
-__device__ inline void chunk_values(const ProxyArgs& a, int row, int c, float* x) {
+__device__ inline ChunkRaw chunk_load(const ProxyArgs& a, int row, int c) {
   const size_t HD = (size_t)a.H * a.D;
+  ChunkRaw r;
   if constexpr (DT == kBF16) {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(a.q) + (size_t)row * HD + (size_t)c * kProxyChunk;
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 8);
+    r.lo = *reinterpret_cast<const i32x4*>(p);
+    r.hi = *reinterpret_cast<const i32x4*>(p + 8);
+    r.s = 1.f;
+  } else {
+    r.lo = *reinterpret_cast<const i32x4*>(a.q + (size_t)row * HD + (size_t)c * kProxyChunk);
+    r.hi = r.lo;
+    r.s = a.q_scale[row];
+  }
+  return r;
+}
+// ... and its 16 values (binary32; fp8 codes times the row scale).
+template <int DT>
+__device__ inline void chunk_values(const ChunkRaw& r, float* x) {
+  if constexpr (DT == kBF16) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[2 * e + 0] = __uint_as_float((uint32_t)lo[e] << 16);
-      x[2 * e + 1] = __uint_as_float((uint32_t)lo[e] & 0xFFFF0000u);
-      x[8 + 2 * e + 0] = __uint_as_float((uint32_t)hi[e] << 16);
-      x[8 + 2 * e + 1] = __uint_as_float((uint32_t)hi[e] & 0xFFFF0000u);
+      x[2 * e + 0] = __uint_as_float((uint32_t)r.lo[e] << 16);
+      x[2 * e + 1] = __uint_as_float((uint32_t)r.lo[e] & 0xFFFF0000u);
+      x[8 + 2 * e + 0] = __uint_as_float((uint32_t)r.hi[e] << 16);
+      x[8 + 2 * e + 1] = __uint_as_float((uint32_t)r.hi[e] & 0xFFFF0000u);
     }
   } else {
-    const i32x4 v = *reinterpret_cast<const i32x4*>(a.q + (size_t)row * HD + (size_t)c * kProxyChunk);
-    const float s = a.q_scale[row];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) x[e] = __fmul_rn(s, e4m3_to_f32((uint8_t)((uint32_t)v[e >> 2] >> (8 * (e & 3)))));
+    for (int e = 0; e < 16; ++e)
+      x[e] = __fmul_rn(r.s, e4m3_to_f32((uint8_t)((uint32_t)r.lo[e >> 2] >> (8 * (e & 3)))));
   }
 }
 
@@ -80,9 +97,19 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
     for (int h = tid; h < a.H; h += kProxyThreads) a.wbar[(size_t)j * a.H + h] = a.w[(size_t)r0 * a.H + h];
     return;
   }
+  // Members are read kProxyU at a time so that their loads are in flight
+  // together (past the last member the load repeats it and is not used; for
+  // the weights +0 is added instead, which leaves a running sum unchanged: a
+  // sum that starts at +0 is never -0).
   for (int h = tid; h < a.H; h += kProxyThreads) {
     float s = 0.f;
-    for (int t = 0; t < n; ++t) s = __fadd_rn(s, a.w[(size_t)(r0 + t) * a.H + h]);
+    for (int t0 = 0; t0 < n; t0 += kProxyU) {
+      float x[kProxyU];
+#pragma unroll
+      for (int u = 0; u < kProxyU; ++u) x[u] = a.w[(size_t)(r0 + min(t0 + u, n - 1)) * a.H + h];
+#pragma unroll
+      for (int u = 0; u < kProxyU; ++u) s = __fadd_rn(s, t0 + u < n ? x[u] : 0.f);
+    }
     a.wbar[(size_t)j * a.H + h] = __fdiv_rn(s, (float)n);
   }
   // means of this thread's chunks, members added in ascending position
@@ -95,11 +122,18 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
     float acc[kProxyChunk];
 #pragma unroll
     for (int e = 0; e < kProxyChunk; ++e) acc[e] = 0.f;
-    for (int t = 0; t < n; ++t) {
-      float x[kProxyChunk];
-      chunk_values<DT>(a, r0 + t, c, x);
+    for (int t0 = 0; t0 < n; t0 += kProxyU) {
+      ChunkRaw raw[kProxyU];
 #pragma unroll
-      for (int e = 0; e < kProxyChunk; ++e) acc[e] = __fadd_rn(acc[e], x[e]);
+      for (int u = 0; u < kProxyU; ++u) raw[u] = chunk_load<DT>(a, r0 + min(t0 + u, n - 1), c);
+#pragma unroll
+      for (int u = 0; u < kProxyU; ++u) {
+        if (t0 + u >= n) break;
+        float x[kProxyChunk];
+        chunk_values<DT>(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < kProxyChunk; ++e) acc[e] = __fadd_rn(acc[e], x[e]);
+      }
     }
 #pragma unroll
     for (int e = 0; e < kProxyChunk; ++e) {
