@@ -6,7 +6,7 @@ lives in pivot_oracle.c (plain single-threaded C, double accumulation); this
 file only marshals numpy arrays.
 
 Pinned functions (see tests/test_oracle_*.py): codecs, score, top-m, dense,
-proxy, Reuse, Refine, decode grouping.  Parity on realistic float inputs is
+proxy, Reuse, Refine, decode grouping, sliding-window union and exclusion.  Parity on realistic float inputs is
 pinned only through invariants and the closed-form/worked examples.
 """
 from __future__ import annotations
@@ -68,6 +68,12 @@ def lib():
                                 C.c_int, i32p, C.c_void_p, C.c_void_p]
         L.orc_prefill_groups.argtypes = [C.POINTER(_View), C.c_int, C.c_int, C.c_int, C.c_int,
                                          C.c_int, i32p, C.c_int, i32p, C.c_void_p]
+        L.orc_dense_rows_ex.argtypes = [C.POINTER(_View), i32p, C.c_int, C.c_int, C.c_int, i32p]
+        L.orc_group_ex.argtypes = [C.POINTER(_View), C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                   C.c_int, C.c_int, i32p, C.c_void_p, C.c_void_p]
+        L.orc_prefill_groups_ex.argtypes = [C.POINTER(_View), C.c_int, C.c_int, C.c_int, C.c_int,
+                                            C.c_int, C.c_int, i32p, C.c_int, i32p, C.c_void_p]
+        L.orc_window_union.argtypes = [i32p, C.c_int, C.c_int, C.c_int, i32p]
         L.orc_score_row.argtypes = [C.POINTER(_View), C.c_int, C.c_int, f64p]
         L.orc_score_pairs.argtypes = [C.POINTER(_View), i32p, i32p, C.c_int, f64p]
         _lib = L
@@ -136,26 +142,38 @@ def proxy(view: View, row0: int, n: int):
     return codes, np.float32(s.value), wbar
 
 
-def dense_rows(view: View, rows, topk_: int):
+def dense_rows(view: View, rows, topk_: int, excl: int = 0):
+    """Dense top-k of the listed rows; excl > 0: row t chooses among 0..t-excl."""
     rows = np.ascontiguousarray(rows, np.int32)
     out = np.empty((rows.shape[0], topk_), np.int32)
-    lib().orc_dense_rows(C.byref(view.c), rows, rows.shape[0], topk_, out)
+    if excl:
+        lib().orc_dense_rows_ex(C.byref(view.c), rows, rows.shape[0], topk_, excl, out)
+    else:
+        lib().orc_dense_rows(C.byref(view.c), rows, rows.shape[0], topk_, out)
     return out
 
 
-def group(view: View, row0: int, pos0: int, n: int, topk_: int, C_: int, mode):
-    """One group; returns (out [n,topk], cand [m] or None, proxy scores [pos0+n])."""
+def group(view: View, row0: int, pos0: int, n: int, topk_: int, C_: int, mode, excl: int = 0):
+    """One group; returns (out [n,topk], cand [m] or None, proxy scores [pos0+n-excl]).
+    excl > 0: the window is excluded, member t chooses among 0..t-excl."""
     mode = MODES.get(mode, mode)
     out = np.empty((n, topk_), np.int32)
     m = C_ if mode == REFINE else topk_
     cand = np.empty(m, np.int32) if mode != DENSE else None
-    psc = np.empty(pos0 + n, np.float64) if mode != DENSE else None
-    lib().orc_group(C.byref(view.c), row0, pos0, n, topk_, C_, mode, out,
-                    _ptr(cand), _ptr(psc))
+    psc = np.empty(max(pos0 + n - excl, 1), np.float64) if mode != DENSE else None
+    if excl:
+        lib().orc_group_ex(C.byref(view.c), row0, pos0, n, topk_, C_, mode, excl, out,
+                           _ptr(cand), _ptr(psc))
+    else:
+        lib().orc_group(C.byref(view.c), row0, pos0, n, topk_, C_, mode, out,
+                        _ptr(cand), _ptr(psc))
+    if psc is not None:
+        psc = psc[:max(pos0 + n - excl, 0)]
     return out, cand, psc
 
 
-def prefill_groups(view: View, L: int, g: int, topk_: int, C_: int, mode, groups):
+def prefill_groups(view: View, L: int, g: int, topk_: int, C_: int, mode, groups,
+                   excl: int = 0):
     """Rows of the listed prefill groups (packed) and their candidate lists."""
     mode = MODES.get(mode, mode)
     groups = np.ascontiguousarray(groups, np.int32)
@@ -163,9 +181,52 @@ def prefill_groups(view: View, L: int, g: int, topk_: int, C_: int, mode, groups
     out = np.empty((nrows, topk_), np.int32)
     m = C_ if mode == REFINE else topk_
     cand = np.empty((groups.shape[0], m), np.int32) if mode != DENSE else None
-    lib().orc_prefill_groups(C.byref(view.c), L, g, topk_, C_, mode, groups, groups.shape[0],
-                             out, _ptr(cand))
+    if excl:
+        lib().orc_prefill_groups_ex(C.byref(view.c), L, g, topk_, C_, mode, excl, groups,
+                                    groups.shape[0], out, _ptr(cand))
+    else:
+        lib().orc_prefill_groups(C.byref(view.c), L, g, topk_, C_, mode, groups,
+                                 groups.shape[0], out, _ptr(cand))
     return out, cand
+
+
+def window_union(sel, positions, W: int):
+    """Sliding window of size W added to selections ([TUT] section on combining
+    the recent window with the selected positions, Figure 3): sel [rows, k]
+    ascending, -1 padded; positions [rows] the queries' positions.  Returns
+    [rows, k + W]: the union, ascending, each position once, -1 padded."""
+    sel = np.ascontiguousarray(sel, np.int32)
+    rows, k = sel.shape
+    out = np.empty((rows, k + W), np.int32)
+    for r in range(rows):
+        o = np.empty(k + W, np.int32)
+        lib().orc_window_union(np.ascontiguousarray(sel[r]), k, int(positions[r]), W, o)
+        out[r] = o
+    return out
+
+
+WINDOW_SHARED, WINDOW_EXCLUDED = 0, 1
+WINDOW_MODES = {"shared": WINDOW_SHARED, "excluded": WINDOW_EXCLUDED}
+
+
+def prefill_window(view: View, L: int, g: int, topk_: int, C_: int, mode, groups, W: int,
+                   wmode):
+    """Listed prefill groups' rows with a sliding window of size W: "shared"
+    (the window's positions stay candidates; union with the selection) or
+    "excluded" (query t chooses among 0..t-W, then the window is added)."""
+    wmode = WINDOW_MODES.get(wmode, wmode)
+    sel, cand = prefill_groups(view, L, g, topk_, C_, mode, groups,
+                               excl=W if wmode == WINDOW_EXCLUDED else 0)
+    return window_union(sel, group_rows(L, g, groups), W), cand
+
+
+def decode_seq_window(dec, b: int, topk_: int, C_: int, mode, W: int, wmode):
+    """decode_seq with a sliding window of size W (see prefill_window)."""
+    wmode = WINDOW_MODES.get(wmode, wmode)
+    n = int(dec.cache_len[b])
+    sel, cand, _ = group(decode_view(dec, b), 0, n - dec.g, dec.g, topk_, C_, mode,
+                         excl=W if wmode == WINDOW_EXCLUDED else 0)
+    return window_union(sel, np.arange(n - dec.g, n), W), cand
 
 
 def group_rows(L: int, g: int, groups):

@@ -281,12 +281,20 @@ void orc_proxy(const orc_view* v, int row0, int n, void* codes_out, float* scale
 
 void orc_dense_rows(const orc_view* v, const int32_t* rows, int nrows, int topk,
                     int32_t* out) {
+  orc_dense_rows_ex(v, rows, nrows, topk, 0, out);
+}
+
+/* Window excluded from the candidates ([TUT] section "최근 window와 선택한
+ * 위치 결합하기", the alternative design): query t chooses among keys
+ * 0..t-excl only (none when t < excl). */
+void orc_dense_rows_ex(const orc_view* v, const int32_t* rows, int nrows, int topk, int excl,
+                       int32_t* out) {
   for (int i = 0; i < nrows; ++i) {
-    int t = rows[i];
-    int n = t + 1;
+    int t = rows[i] - excl;
+    int n = t + 1 > 0 ? t + 1 : 0;
     double* sc = (double*)malloc(sizeof(double) * (size_t)n);
     int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
-    orc_score_row(v, t, n, sc);
+    orc_score_row(v, rows[i], n, sc);
     for (int s = 0; s < n; ++s) pos[s] = s;
     orc_topk(n, pos, sc, topk, out + (long)i * topk);
     free(sc);
@@ -304,19 +312,29 @@ void orc_dense_rows(const orc_view* v, const int32_t* rows, int nrows, int topk,
 
 void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, int mode,
                int32_t* out, int32_t* cand_out, double* proxy_scores_out) {
+  orc_group_ex(v, row0, pos0, n, topk, C, mode, 0, out, cand_out, proxy_scores_out);
+}
+
+/* The same with the window excluded from the candidates ([TUT] section
+ * "최근 window와 선택한 위치 결합하기", the alternative design).  Reading for
+ * a group: member t chooses among positions 0..t-excl, so the proxy's scan,
+ * which serves every member, covers 0..e-excl (the last member's range). */
+void orc_group_ex(const orc_view* v, int row0, int pos0, int n, int topk, int C, int mode,
+                  int excl, int32_t* out, int32_t* cand_out, double* proxy_scores_out) {
   const int H = v->H, D = v->D;
-  const int e = pos0 + n - 1; /* last member's position */
-  const int nk = e + 1;       /* keys 0..e */
+  const int e = pos0 + n - 1 - excl; /* last position any member may choose */
+  const int nk = e + 1 > 0 ? e + 1 : 0; /* keys 0..e */
 
   if (mode == ORC_DENSE) {
     for (int i = 0; i < n; ++i) {
-      int t = pos0 + i;
-      double* sc = (double*)malloc(sizeof(double) * (size_t)(t + 1));
-      int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(t + 1));
+      int t = pos0 + i - excl;
+      int nt = t + 1 > 0 ? t + 1 : 0;
+      double* sc = (double*)malloc(sizeof(double) * (size_t)(nt + 1));
+      int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nt + 1));
       const void* qc = code_ptr(v->dtype, v->q, (long)(row0 + i) * H * D);
-      score_keys(v, qc, row_scale(v, row0 + i), v->w + (long)(row0 + i) * H, NULL, t + 1, sc);
-      for (int s = 0; s <= t; ++s) pos[s] = s;
-      orc_topk(t + 1, pos, sc, topk, out + (long)i * topk);
+      score_keys(v, qc, row_scale(v, row0 + i), v->w + (long)(row0 + i) * H, NULL, nt, sc);
+      for (int s = 0; s < nt; ++s) pos[s] = s;
+      orc_topk(nt, pos, sc, topk, out + (long)i * topk);
       free(sc);
       free(pos);
     }
@@ -329,8 +347,8 @@ void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, in
   float* pw = (float*)malloc(sizeof(float) * (size_t)H);
   orc_proxy(v, row0, n, pq, &ps, pw);
 
-  double* psc = (double*)malloc(sizeof(double) * (size_t)nk);
-  int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)nk);
+  double* psc = (double*)malloc(sizeof(double) * (size_t)(nk + 1));
+  int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nk + 1));
   score_keys(v, pq, ps, pw, NULL, nk, psc);
   for (int s = 0; s < nk; ++s) pos[s] = s;
   if (proxy_scores_out) memcpy(proxy_scores_out, psc, sizeof(double) * (size_t)nk);
@@ -340,7 +358,7 @@ void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, in
     orc_topk(nk, pos, psc, topk, ptop);
     if (cand_out) memcpy(cand_out, ptop, sizeof(int32_t) * (size_t)topk);
     for (int i = 0; i < n; ++i) {
-      int t = pos0 + i;
+      int t = pos0 + i - excl;
       int32_t* o = out + (long)i * topk;
       int c = 0;
       for (int j = 0; j < topk; ++j)
@@ -355,7 +373,7 @@ void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, in
     double* msc = (double*)malloc(sizeof(double) * (size_t)C);
     int32_t* mpos = (int32_t*)malloc(sizeof(int32_t) * (size_t)C);
     for (int i = 0; i < n; ++i) {
-      int t = pos0 + i;
+      int t = pos0 + i - excl;
       const void* qc = code_ptr(v->dtype, v->q, (long)(row0 + i) * H * D);
       int np = 0;
       for (int j = 0; j < C; ++j)
@@ -379,14 +397,43 @@ void orc_group(const orc_view* v, int row0, int pos0, int n, int topk, int C, in
 void orc_prefill_groups(const orc_view* v, int L, int g, int topk, int C, int mode,
                         const int32_t* groups, int ngroups, int32_t* out_rows,
                         int32_t* cand_out) {
+  orc_prefill_groups_ex(v, L, g, topk, C, mode, 0, groups, ngroups, out_rows, cand_out);
+}
+
+void orc_prefill_groups_ex(const orc_view* v, int L, int g, int topk, int C, int mode, int excl,
+                           const int32_t* groups, int ngroups, int32_t* out_rows,
+                           int32_t* cand_out) {
   int m = mode == ORC_REFINE ? C : topk;
   long row = 0;
   for (int i = 0; i < ngroups; ++i) {
     int j = groups[i];
     int first = j * g;
     int n = (first + g <= L) ? g : L - first;
-    orc_group(v, first, first, n, topk, C, mode, out_rows + row * topk,
-              cand_out ? cand_out + (long)i * m : NULL, NULL);
+    orc_group_ex(v, first, first, n, topk, C, mode, excl, out_rows + row * topk,
+                 cand_out ? cand_out + (long)i * m : NULL, NULL);
     row += n;
   }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sliding window added to a selection ([TUT] section "최근 window와 선택한  */
+/* 위치 결합하기", Figure 3): the window of size W at position t holds the   */
+/* positions max(0, t-W+1) .. t; the positions read are the union of the     */
+/* window and the selection, each position once.  Output: ascending,        */
+/* padded with -1 to k + W entries.                                          */
+/* ------------------------------------------------------------------------ */
+
+void orc_window_union(const int32_t* sel, int k, int t, int W, int32_t* out) {
+  int32_t* all = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k + W + 1));
+  int n = 0;
+  for (int i = 0; i < k; ++i)
+    if (sel[i] >= 0) all[n++] = sel[i];
+  for (int s = t - W + 1; s <= t; ++s)
+    if (s >= 0) all[n++] = s;
+  qsort(all, (size_t)n, sizeof(int32_t), by_int_asc);
+  int c = 0;
+  for (int i = 0; i < n; ++i)
+    if (c == 0 || all[i] != out[c - 1]) out[c++] = all[i];
+  for (; c < k + W; ++c) out[c] = -1;
+  free(all);
 }

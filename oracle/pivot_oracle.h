@@ -90,6 +90,23 @@ void orc_prefill_groups(const orc_view* v, int L, int g, int topk, int C, int mo
                         const int32_t* groups, int ngroups, int32_t* out_rows,
                         int32_t* cand_out);
 
+/* Variants with the sliding window excluded from the candidates: every query
+ * at position t chooses among positions 0..t-excl only, and a group's proxy
+ * scan covers 0..e-excl (e = its last member's position).  excl = 0 gives the
+ * functions above. */
+void orc_dense_rows_ex(const orc_view* v, const int32_t* rows, int nrows, int topk, int excl,
+                       int32_t* out);
+void orc_group_ex(const orc_view* v, int row0, int pos0, int n, int topk, int C, int mode,
+                  int excl, int32_t* out, int32_t* cand_out, double* proxy_scores_out);
+void orc_prefill_groups_ex(const orc_view* v, int L, int g, int topk, int C, int mode, int excl,
+                           const int32_t* groups, int ngroups, int32_t* out_rows,
+                           int32_t* cand_out);
+
+/* Union of a selection sel [k] (ascending, -1 padded) with the sliding window
+ * of size W at position t (positions max(0, t-W+1)..t): ascending, each
+ * position once, -1 padded to k + W entries. */
+void orc_window_union(const int32_t* sel, int k, int t, int W, int32_t* out);
+
 /* Scores of the query row `row` of the view against keys [0, n). */
 void orc_score_row(const orc_view* v, int row, int n, double* out);
 

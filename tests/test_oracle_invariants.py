@@ -130,3 +130,54 @@ def test_decode_group_equals_last_prefill_group():  # I11
             assert np.array_equal(out, rows)
             if mode != "dense":
                 assert np.array_equal(dc, cand[0])
+
+
+# ----------------------------------------------------------------------------
+# sliding window (tutorial "Sparse Attention의 Indexer", section on combining
+# the recent window with the selected positions): the shared window is a union,
+# the excluded window moves every query's limit from t to t - W
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W", [1, 3, 7])
+def test_window_excluded_identities(case, W):
+    L, k, inp, v, dense = case
+    dense_x = oracle.dense_rows(v, np.arange(L), k, excl=W)
+    for t in range(L):
+        r = dense_x[t][dense_x[t] >= 0]
+        assert np.all(r <= t - W) and len(r) == min(k, max(0, t - W + 1))
+    for g in (1, 2, 3, 8):
+        rows, _ = _all_groups_x(v, L, g, k, L, "refine", W)
+        assert np.array_equal(rows, dense_x)                   # I2 with the window excluded
+    rows, _ = _all_groups_x(v, L, 1, k, k, "reuse", W)
+    assert np.array_equal(rows, dense_x)                       # I3 with the window excluded
+    for g in (2, 5):
+        ref, _ = _all_groups_x(v, L, g, k, k + g - 1 + 2, "refine", W)
+        for t in range(L):
+            r = ref[t][ref[t] >= 0]
+            assert np.all(r <= t - W) and len(r) == min(k, max(0, t - W + 1))
+
+
+def _all_groups_x(v, L, g, k, C_, mode, W):
+    G = (L + g - 1) // g
+    return oracle.prefill_groups(v, L, g, k, C_, mode, np.arange(G), excl=W)
+
+
+@pytest.mark.parametrize("W", [1, 4, 9])
+def test_window_union_structure(case, W):
+    L, k, inp, v, dense = case
+    for mode, g in (("refine", 3), ("reuse", 4)):
+        sel, _ = _all_groups(v, L, g, k, k + g + 1, mode)
+        out = oracle.window_union(sel, np.arange(L), W)
+        assert out.shape == (L, k + W)
+        for t in range(L):
+            lo = max(0, t - W + 1)
+            r = out[t][out[t] >= 0]
+            assert np.all(np.diff(r) > 0) and np.all(out[t][len(r):] == -1)
+            s = sel[t][sel[t] >= 0]
+            assert r.tolist() == s[s < lo].tolist() + list(range(lo, t + 1))
+    # with the window excluded the union is disjoint: every k + W slot is used
+    # once the prefix is long enough
+    sel, _ = _all_groups_x(v, L, 2, k, L, "refine", W)
+    out = oracle.window_union(sel, np.arange(L), W)
+    for t in range(L):
+        assert np.sum(out[t] >= 0) == min(k, max(0, t - W + 1)) + min(W, t + 1)

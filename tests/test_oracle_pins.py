@@ -118,6 +118,50 @@ def test_worked_example_as_one_decode_group():
 
 
 # ----------------------------------------------------------------------------
+# sliding window added to the selection (printed Figure 3 union; the
+# excluded-window design derived by hand from the printed Figure 1 scores)
+# ----------------------------------------------------------------------------
+
+def _window_example():
+    return json.load(open(os.path.join(GOLDEN, "window_example_fig3.json")))
+
+
+def test_window_union_printed_example():
+    ex, v = _fig1_view()
+    wx = _window_example()
+    W = wx["window"]
+    sel = oracle.dense_rows(v, [7, 6], ex["topk"])
+    out = oracle.window_union(sel, [7, 6], W)
+    assert out.shape == (2, ex["topk"] + W)
+    got7 = [int(p) for p in out[0] if p >= 0]
+    assert got7 == wx["union_p7_printed"]
+    assert len(got7) == wx["positions_read_p7_printed"]  # 7 is read once
+    assert set(wx["window_p7"]) <= set(got7)
+    assert out[0].tolist()[len(got7):] == [-1] * (ex["topk"] + W - len(got7))
+    assert [int(p) for p in out[1] if p >= 0] == wx["union_p6_derived"]
+    # window 0 leaves a selection unchanged; window 1 adds the query's own position
+    assert oracle.window_union(sel, [7, 6], 0).tolist() == sel.tolist()
+    assert [int(p) for p in oracle.window_union(sel, [7, 6], 1)[1] if p >= 0] == [1, 3, 6]
+
+
+def test_window_excluded_derived_example():
+    ex, v = _fig1_view()
+    wx = _window_example()
+    W = wx["window"]
+    sel = oracle.dense_rows(v, [7, 6], ex["topk"], excl=W)
+    out = oracle.window_union(sel, [7, 6], W)
+    assert out[0].tolist() == wx["excluded_p7_derived"]  # all k + W slots used
+    assert out[1].tolist() == wx["excluded_p6_derived"]
+    # as one decode group (p6, p7): the same rows
+    rows, _, _ = oracle.group(v, 6, 6, 2, ex["topk"], ex["topk"], "dense", excl=W)
+    assert rows.tolist() == sel[::-1].tolist()
+    # a window as long as the prefix leaves nothing to choose
+    assert oracle.dense_rows(v, [2], 3, excl=3).tolist() == [[-1, -1, -1]]
+    assert oracle.window_union(oracle.dense_rows(v, [2], 3, excl=3), [2], 3).tolist() == \
+        [[0, 1, 2, -1, -1, -1]]
+
+
+# ----------------------------------------------------------------------------
 # hand-derived PIVOT example (integers, exact)
 # ----------------------------------------------------------------------------
 
@@ -321,3 +365,39 @@ def test_tiny_config_scores_are_exact_multiples():
         assert np.all(s * 2 ** 9 == np.round(s * 2 ** 9))
         assert np.all(np.abs(s) < 2 ** 6)
         assert np.array_equal(s.astype(np.float32).astype(np.float64), s)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_window_excluded_bruteforce_tiny(seed):
+    """With the window excluded, dense and Refine rows are the brute-force
+    selection over positions 0..t-W; the proxy's candidates over 0..e-W."""
+    rng = np.random.default_rng(300 + seed)
+    L = int(rng.integers(3, 10))
+    H = int(rng.integers(1, 3))
+    D = int(rng.integers(1, 4))
+    inp = synth.small_integer(L, H, D, seed=400 + seed, qmax=2, kmax=2, wmax=2)
+    v = oracle.View.of(inp)
+    k = int(rng.integers(1, 5))
+    W = int(rng.integers(1, 4))
+    dense = oracle.dense_rows(v, np.arange(L), k, excl=W)
+    for t in range(L):
+        n = max(t - W + 1, 0)
+        sc = oracle.score_row(v, t, n) if n else []
+        assert dense[t].tolist() == _brute_topk(list(sc), list(range(n)), k)
+    for g in range(1, L + 1):
+        C_ = k + int(rng.integers(0, 3))
+        G = (L + g - 1) // g
+        rows, cand = oracle.prefill_groups(v, L, g, k, C_, "refine", np.arange(G), excl=W)
+        r = 0
+        for j in range(G):
+            members = range(j * g, min(L, j * g + g))
+            ne = max(members[-1] - W + 1, 0)
+            pq, ps, pw = oracle.proxy(v, j * g, len(members))
+            pv = oracle.View("bf16", pq[None], None, pw[None], inp.k, None)
+            psc = oracle.score_row(pv, 0, ne) if ne else []
+            assert cand[j].tolist() == _brute_topk(list(psc), list(range(ne)), C_)
+            for t in members:
+                pool = [c for c in cand[j] if 0 <= c <= t - W]
+                sc = oracle.score_pairs(v, [t] * len(pool), pool) if pool else []
+                assert rows[r].tolist() == _brute_topk(list(sc), pool, k)
+                r += 1
