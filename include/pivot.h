@@ -74,6 +74,11 @@ typedef enum {
 
 typedef enum { PIVOT_BF16 = 0, PIVOT_FP8_E4M3 = 1 } pivot_dtype_t;
 
+typedef enum {
+  PIVOT_WINDOW_SHARED = 0,   /* the window's positions remain candidates; union with the selection */
+  PIVOT_WINDOW_EXCLUDED = 1  /* the window is excluded from the candidates; topk chosen before it */
+} pivot_window_mode_t;
+
 int pivot_version(void);
 const char* pivot_status_string(int status);
 const char* pivot_last_error(void);
@@ -117,6 +122,38 @@ int pivot_indexer_decode(const void* q, const float* q_scale, const float* w,
                          int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
                          int dtype, int32_t* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prefill and decode with a sliding window added to every query's selection
+ * (tutorial "Sparse Attention의 Indexer", section on combining the recent
+ * window with the selected positions, Figure 3).  The window of size `window`
+ * at position t holds the positions max(0, t-window+1) .. t; each query reads
+ * the union of its window and its selection, each position once.
+ *
+ *   window_mode PIVOT_WINDOW_SHARED: the selection is the one pivot_indexer /
+ *     pivot_indexer_decode make (the window's positions stay candidates), so
+ *     a row holds up to topk + window positions and fewer when they overlap.
+ *   window_mode PIVOT_WINDOW_EXCLUDED: the window is excluded from the
+ *     candidates, so a query at t chooses its topk among 0..t-window; for a
+ *     group the proxy's scan covers 0..e-window (e = its last member) and
+ *     every member keeps the candidates <= its own t-window.  A row holds
+ *     min(topk, max(0, t-window+1)) + min(window, t+1) positions.
+ *
+ * Arguments as for pivot_indexer / pivot_indexer_decode, plus window >= 0
+ * and window_mode; out is [L][topk + window] (prefill) or
+ * [B][g][topk + window] (decode), ascending, -1 padded.  The workspace sizes
+ * are those of the calls without a window.  window = 0 with either mode gives
+ * the rows of the calls without a window.
+ * ------------------------------------------------------------------------- */
+int pivot_indexer_window(const void* q, const float* q_scale, const float* w, const void* k,
+                         const float* k_scale, int L, int H, int D, int g, int topk, int C,
+                         int mode, int dtype, int window, int window_mode, int32_t* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int pivot_indexer_decode_window(const void* q, const float* q_scale, const float* w,
+                                const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                                int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                                int dtype, int window, int window_mode, int32_t* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Single steps of the prefill path, for step-level checks.
@@ -166,7 +203,8 @@ enum {
   PIVOT_K_MEMBER_SELECT = 4,/* Refine member top-k */
   PIVOT_K_BROADCAST = 5,    /* Reuse broadcast */
   PIVOT_K_DECODE_SCAN = 6,  /* decode key-cache scan */
-  PIVOT_K_COUNT = 7
+  PIVOT_K_WINDOW = 7,       /* sliding-window union */
+  PIVOT_K_COUNT = 8
 };
 int pivot_profile_enable(int on);
 int pivot_profile_read(double* ms, long long* launches, int n);

@@ -116,3 +116,27 @@ def test_python_binding_fails_loudly_without_device():
     with pytest.raises(pv.PivotError):
         pv.indexer(q, torch.zeros((16, 4)), torch.zeros((16, 32), dtype=torch.bfloat16), g=4,
                    topk=4, C=8)
+
+
+def test_window_validation(lib):
+    # the window entry points check window and window_mode before anything runs
+    def pre(window, wmode, **kw):
+        a = dict(q=FAKE, w=FAKE, k=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.pivot_indexer_window(a["q"], None, a["w"], a["k"], None, 2048, 4, 32, 4, 64,
+                                        256, pv.REFINE, 0, window, wmode, a["out"], a["ws"],
+                                        a["wsb"], None)
+
+    def dec(window, wmode, **kw):
+        a = dict(out=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.pivot_indexer_decode_window(FAKE, None, FAKE, FAKE, None, FAKE, 32, 131072, 64,
+                                               128, 2, 2048, 4096, pv.REFINE, 0, window, wmode,
+                                               a["out"], FAKE, a["wsb"], None)
+    for f in (pre, dec):
+        assert f(-1, 0) == ERR_PARAM
+        assert f(3, 2) == ERR_PARAM
+        assert f(3, -1) == ERR_PARAM
+        assert f(1 << 30, 1) == ERR_PARAM
+        assert f(3, 0, out=None) == ERR_NULL
+        assert f(3, 1, wsb=100) == ERR_WORKSPACE  # valid window: fails only on the workspace

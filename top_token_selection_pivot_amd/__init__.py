@@ -74,6 +74,10 @@ def load():
     L.pivot_decode_workspace_size.argtypes = [i] * 9
     L.pivot_indexer_decode.restype = i
     L.pivot_indexer_decode.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, vp, sz, vp]
+    L.pivot_indexer_window.restype = i
+    L.pivot_indexer_window.argtypes = [vp, fp, fp, vp, fp] + [i] * 10 + [ip, vp, sz, vp]
+    L.pivot_indexer_decode_window.restype = i
+    L.pivot_indexer_decode_window.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 11 + [ip, vp, sz, vp]
     L.pivot_decode_candidates.restype = i
     L.pivot_decode_candidates.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, vp, sz, vp]
     L.pivot_profile_enable.restype = i
@@ -146,13 +150,23 @@ def _workspace(nbytes: int, device, workspace, min_bytes: Optional[int] = None):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+WINDOW_MODES = {"shared": 0, "excluded": 1}
+
+
+def _window_mode(wm) -> int:
+    return WINDOW_MODES[wm] if isinstance(wm, str) else int(wm)
+
+
 def indexer(q, w, k, *, g: int, topk: int, C: int = 0, mode="refine", q_scale=None,
-            k_scale=None, out=None, workspace=None, stream=None) -> torch.Tensor:
+            k_scale=None, out=None, workspace=None, stream=None, window: int = 0,
+            window_mode="shared") -> torch.Tensor:
     """Prefill indexer for one sequence.
 
     q [L,H,D] bf16 or fp8 codes, w [L,H] float32, k [L,D] codes; fp8 needs
     q_scale [L] and k_scale [L] float32.  Returns int32 [L, topk]: ascending
-    selected positions, -1 padded.
+    selected positions, -1 padded.  window > 0 adds the sliding window of that
+    size to every row (window_mode "shared" or "excluded", as in
+    pivot_indexer_window) and returns [L, topk + window].
     """
     L = load()
     q, w, k = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k, "k")
@@ -161,12 +175,17 @@ def indexer(q, w, k, *, g: int, topk: int, C: int = 0, mode="refine", q_scale=No
     dt = _dtype_of(q)
     m = _mode(mode)
     if out is None:
-        out = torch.empty((Lq, topk), dtype=torch.int32, device=q.device)
+        out = torch.empty((Lq, topk + window), dtype=torch.int32, device=q.device)
     ws = _workspace(L.pivot_workspace_size(Lq, H, D, g, topk, C, m, dt), q.device, workspace,
                     L.pivot_workspace_min_size(Lq, H, D, g, topk, C, m, dt))
-    _check(L.pivot_indexer(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), Lq, H, D, g,
-                           topk, C, m, dt, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                           _stream(stream)))
+    nbytes = ws.numel() * ws.element_size()
+    if window:
+        _check(L.pivot_indexer_window(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), Lq,
+                                      H, D, g, topk, C, m, dt, window, _window_mode(window_mode),
+                                      _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check(L.pivot_indexer(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), Lq, H, D,
+                               g, topk, C, m, dt, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
     return out
 
 
@@ -205,10 +224,10 @@ def proxy_mean(q, w, g: int, q_scale=None, stream=None):
 
 def indexer_decode(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="refine",
                    q_scale=None, k_scale=None, out=None, workspace=None,
-                   stream=None) -> torch.Tensor:
+                   stream=None, window: int = 0, window_mode="shared") -> torch.Tensor:
     """One MTP decode step: q [B,g,H,D], w [B,g,H], k_cache [B,Lmax,D],
     cache_len [B] int32 (device); fp8 needs q_scale [B,g], k_scale [B,Lmax].
-    Returns int32 [B, g, topk]."""
+    Returns int32 [B, g, topk] ([B, g, topk + window] with a window)."""
     L = load()
     q, w, k_cache = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k_cache, "k_cache")
     cache_len = _dev(cache_len, "cache_len", torch.int32)
@@ -217,12 +236,19 @@ def indexer_decode(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="ref
     dt = _dtype_of(q)
     m = _mode(mode)
     if out is None:
-        out = torch.empty((B, g, topk), dtype=torch.int32, device=q.device)
+        out = torch.empty((B, g, topk + window), dtype=torch.int32, device=q.device)
     ws = _workspace(L.pivot_decode_workspace_size(B, Lmax, H, D, g, topk, C, m, dt), q.device,
                     workspace)
-    _check(L.pivot_indexer_decode(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale),
-                                  _ptr(cache_len), B, Lmax, H, D, g, topk, C, m, dt, _ptr(out),
-                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    nbytes = ws.numel() * ws.element_size()
+    if window:
+        _check(L.pivot_indexer_decode_window(
+            _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(cache_len), B,
+            Lmax, H, D, g, topk, C, m, dt, window, _window_mode(window_mode), _ptr(out), _ptr(ws),
+            nbytes, _stream(stream)))
+    else:
+        _check(L.pivot_indexer_decode(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache),
+                                      _ptr(k_scale), _ptr(cache_len), B, Lmax, H, D, g, topk, C, m,
+                                      dt, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
     return out
 
 
@@ -255,7 +281,7 @@ def selftest_mfma_layout(device="cuda") -> torch.Tensor:
 
 
 KERNEL_CLASSES = ("proxy_mean", "scan", "select", "refine_score", "member_select", "broadcast",
-                  "decode_scan")
+                  "decode_scan", "window")
 
 
 def profile_enable(on: bool = True) -> None:

@@ -119,6 +119,14 @@ int validate_common(const void* q, const float* q_scale, const float* w, const v
   return PIVOT_OK;
 }
 
+int validate_window(int window, int wmode, int topk) {
+  if (wmode != PIVOT_WINDOW_SHARED && wmode != PIVOT_WINDOW_EXCLUDED)
+    return fail(PIVOT_ERR_PARAM, "window_mode %d is not SHARED or EXCLUDED", wmode);
+  if (window < 0) return fail(PIVOT_ERR_PARAM, "window=%d must be >= 0", window);
+  if ((long long)topk + window > (1ll << 30)) return fail(PIVOT_ERR_PARAM, "topk + window too large");
+  return PIVOT_OK;
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PIVOT_OK;
   return fail(PIVOT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -184,9 +192,14 @@ struct ProfileScope {
 int run_prefill(const void* q, const float* q_scale, const float* w, const void* k,
                 const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
                 int dtype, int32_t* out, int32_t* cand_user, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, int window = 0, int wmode = 0) {
   int st = validate_common(q, q_scale, w, k, k_scale, H, D, g, topk, C, mode, dtype);
   if (st) return st;
+  st = validate_window(window, wmode, topk);
+  if (st) return st;
+  // window excluded from the candidates: every limit moves down by the window
+  const int excl = wmode == PIVOT_WINDOW_EXCLUDED ? window : 0;
+  const long long ldo = (long long)topk + window;
   if (L < 1) return fail(PIVOT_ERR_SHAPE, "L=%d must be >= 1", L);
   if ((long long)L * H * D > (1ll << 40)) return fail(PIVOT_ERR_SHAPE, "L*H*D too large");
   if ((long long)L * D * esize(dtype) >= (1ll << 31))
@@ -222,10 +235,11 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
     const int r1 = std::min(p.G, r0 + CR);
     ScanArgs sa{};
     if (dense) {
-      sa = ScanArgs{qb, q_scale, w, kb, k_scale, L, H, r0, r1, 1, 0, L - 1, kScanKeyChunk, S, p.ldS};
-    } else {
-      sa = ScanArgs{qbar, qbs, wbar, kb, k_scale, L, H, r0, r1, g, g - 1, L - 1, kScanKeyChunk, S,
+      sa = ScanArgs{qb, q_scale, w, kb, k_scale, L, H, r0, r1, 1, -excl, L - 1 - excl, kScanKeyChunk, S,
                     p.ldS};
+    } else {
+      sa = ScanArgs{qbar, qbs, wbar, kb, k_scale, L, H, r0, r1, g, g - 1 - excl, L - 1 - excl, kScanKeyChunk,
+                    S, p.ldS};
     }
     // the scan runs in launches of at most kScanRowsPerLaunch rows (measured
     // faster than one launch per pass at 16K-128K, bf16 and fp8)
@@ -243,12 +257,12 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
     ta.nrows = r1 - r0;
     ta.kind = kLenPos;
     ta.pos_mul = dense ? 1 : g;
-    ta.pos_add = dense ? 0 : g - 1;
-    ta.pos_cap = L - 1;
+    ta.pos_add = (dense ? 0 : g - 1) - excl;
+    ta.pos_cap = L - 1 - excl;
     if (dense) {
       ta.m = topk;
-      ta.out = out + (size_t)r0 * topk;
-      ta.ldo = topk;
+      ta.out = out + (size_t)r0 * ldo;
+      ta.ldo = ldo;
       PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "dense top-k");
       continue;
     }
@@ -260,12 +274,12 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
     if (cand_user) continue;
     const int row_begin = r0 * g, row_end = std::min(L, r1 * g);
     if (mode == PIVOT_MODE_REUSE) {
-      BroadcastArgs ba{cdst, p.m, r0, out + (size_t)row_begin * topk, topk, 0, g, 0, nullptr,
-                       row_begin, row_end};
+      BroadcastArgs ba{cdst, p.m, r0, out + (size_t)row_begin * ldo, topk, 0, g, 0, nullptr,
+                       row_begin, row_end, ldo, excl};
       PIVOT_LAUNCH_K(PIVOT_K_BROADCAST, s, launch_broadcast(ba, s), "reuse broadcast");
     } else {
       RefineArgs ra{qb, q_scale, w, kb, k_scale, H, 0, L, g, 0, nullptr, r0, r1, cdst, p.m, p.m,
-                    kRefineSlotChunk, S, p.ldR, row_begin};
+                    kRefineSlotChunk, S, p.ldR, row_begin, excl};
       PIVOT_LAUNCH_K(PIVOT_K_REFINE, s, launch_refine(ra, dtype, D, s), "refine score");
       TopkArgs tr{};
       tr.S = S;
@@ -273,8 +287,9 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
       tr.row_begin = row_begin;
       tr.nrows = row_end - row_begin;
       tr.m = topk;
-      tr.out = out + (size_t)row_begin * topk;
-      tr.ldo = topk;
+      tr.out = out + (size_t)row_begin * ldo;
+      tr.ldo = ldo;
+      tr.excl = excl;
       tr.kind = kLenRefine;
       tr.decode = 0;
       tr.g = g;
@@ -283,6 +298,10 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
       tr.map_grp_begin = r0;
       PIVOT_LAUNCH_K(PIVOT_K_MEMBER_SELECT, s, launch_topk(tr, s), "refine top-k");
     }
+  }
+  if (window > 0 && !cand_user) {
+    WindowArgs wa{out, ldo, L, topk, window, 0, g, 0, nullptr, 0};
+    PIVOT_LAUNCH_K(PIVOT_K_WINDOW, s, launch_window_union(wa, s), "window union");
   }
   return PIVOT_OK;
 }
@@ -414,9 +433,13 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
                       const void* k_cache, const float* k_scale, const int32_t* cache_len,
                       int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
                       int dtype, int32_t* out, int32_t* cand_user, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, int window = 0, int wmode = 0) {
   int st = validate_common(q, q_scale, w, k_cache, k_scale, H, D, g, topk, C, mode, dtype);
   if (st) return st;
+  st = validate_window(window, wmode, topk);
+  if (st) return st;
+  const int excl = wmode == PIVOT_WINDOW_EXCLUDED ? window : 0;
+  const long long ldo = (long long)topk + window;
   if (B < 1 || Lmax < 1) return fail(PIVOT_ERR_SHAPE, "B=%d and Lmax=%d must be >= 1", B, Lmax);
   if (g > Lmax) return fail(PIVOT_ERR_PARAM, "g=%d exceeds Lmax=%d", g, Lmax);
   if ((long long)B * Lmax * D > (1ll << 40)) return fail(PIVOT_ERR_SHAPE, "B*Lmax*D too large");
@@ -440,17 +463,19 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   uint32_t* hist = (uint32_t*)(ws + p.off_hist);
   DecSelectArgs sel{S, p.ldS, p.rows, 0, 0, g, Lmax, cache_len, hist, p.parts,
                     (uint32_t*)(ws + p.off_ckey), (int32_t*)(ws + p.off_cslot), (int32_t*)(ws + p.off_ccount),
-                    nullptr, 0};
+                    nullptr, 0, excl};
+  const WindowArgs wa{out, ldo, B * g, topk, window, 1, g, Lmax, cache_len, 0};
   if (mode == PIVOT_MODE_DENSE) {
     PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_fill_u32(hist, (size_t)p.rows * kSelectBins1, 0u, s),
                    "decode histogram clear");
-    DecScanArgs da{qb, q_scale, w, kb, k_scale, Lmax, H, cache_len, g, g, S, p.ldS, hist, B};
+    DecScanArgs da{qb, q_scale, w, kb, k_scale, Lmax, H, cache_len, g, g, S, p.ldS, hist, B, excl};
     PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");
     sel.m = topk;
     sel.kind = kLenDecodeDense;
     sel.out = out;
-    sel.ldo = topk;
+    sel.ldo = ldo;
     PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_decode_select(sel, s), "decode dense top-k");
+    if (window > 0) PIVOT_LAUNCH_K(PIVOT_K_WINDOW, s, launch_window_union(wa, s), "window union");
     return PIVOT_OK;
   }
   uint8_t* qbar = ws + p.off_qbar;
@@ -460,7 +485,7 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   // the proxy kernel also clears the scan's histograms
   ProxyArgs pa{qb, q_scale, w, B * g, H, D, g, qbar, qbs, wbar, hist, (size_t)p.rows * kSelectBins1};
   PIVOT_LAUNCH_K(PIVOT_K_PROXY, s, launch_proxy_mean(pa, dtype, s), "decode proxy mean");
-  DecScanArgs da{qbar, qbs, wbar, kb, k_scale, Lmax, H, cache_len, g, 1, S, p.ldS, hist, B};
+  DecScanArgs da{qbar, qbs, wbar, kb, k_scale, Lmax, H, cache_len, g, 1, S, p.ldS, hist, B, excl};
   PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");
   sel.m = p.m;
   sel.kind = kLenCache;
@@ -469,13 +494,14 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_decode_select(sel, s), "decode proxy top-m");
   if (cand_user) return PIVOT_OK;
   if (mode == PIVOT_MODE_REUSE) {
-    BroadcastArgs ba{cand, p.m, 0, out, topk, 1, g, Lmax, cache_len, 0, B * g};
+    BroadcastArgs ba{cand, p.m, 0, out, topk, 1, g, Lmax, cache_len, 0, B * g, ldo, excl};
     PIVOT_LAUNCH_K(PIVOT_K_BROADCAST, s, launch_broadcast(ba, s), "decode reuse broadcast");
+    if (window > 0) PIVOT_LAUNCH_K(PIVOT_K_WINDOW, s, launch_window_union(wa, s), "window union");
     return PIVOT_OK;
   }
   float* R = (float*)(ws + p.off_R);
   RefineArgs ra{qb, q_scale, w, kb, k_scale, H, 1, 0, g, Lmax, cache_len, 0, B, cand, p.m, p.m,
-                kRefineSlotChunk, R, p.ldR, 0};
+                kRefineSlotChunk, R, p.ldR, 0, excl};
   PIVOT_LAUNCH_K(PIVOT_K_REFINE, s, launch_refine(ra, dtype, D, s), "decode refine score");
   TopkArgs tr{};
   tr.S = R;
@@ -484,7 +510,8 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   tr.nrows = B * g;
   tr.m = topk;
   tr.out = out;
-  tr.ldo = topk;
+  tr.ldo = ldo;
+  tr.excl = excl;
   tr.kind = kLenRefine;
   tr.decode = 1;
   tr.g = g;
@@ -494,6 +521,7 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   tr.ldmap = p.m;
   tr.map_grp_begin = 0;
   PIVOT_LAUNCH_K(PIVOT_K_MEMBER_SELECT, s, launch_topk(tr, s), "decode refine top-k");
+  if (window > 0) PIVOT_LAUNCH_K(PIVOT_K_WINDOW, s, launch_window_union(wa, s), "window union");
   return PIVOT_OK;
 }
 
@@ -505,6 +533,25 @@ int pivot_indexer_decode(const void* q, const float* q_scale, const float* w,
   if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
   return run_decode(q, q_scale, w, k_cache, k_scale, cache_len, B, Lmax, H, D, g, topk, C, mode,
                     dtype, out, nullptr, workspace, workspace_bytes, stream);
+}
+
+int pivot_indexer_window(const void* q, const float* q_scale, const float* w, const void* k,
+                         const float* k_scale, int L, int H, int D, int g, int topk, int C,
+                         int mode, int dtype, int window, int window_mode, int32_t* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  return run_prefill(q, q_scale, w, k, k_scale, L, H, D, g, topk, C, mode, dtype, out, nullptr,
+                     workspace, workspace_bytes, stream, window, window_mode);
+}
+
+int pivot_indexer_decode_window(const void* q, const float* q_scale, const float* w,
+                                const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                                int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                                int dtype, int window, int window_mode, int32_t* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  return run_decode(q, q_scale, w, k_cache, k_scale, cache_len, B, Lmax, H, D, g, topk, C, mode,
+                    dtype, out, nullptr, workspace, workspace_bytes, stream, window, window_mode);
 }
 
 int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,

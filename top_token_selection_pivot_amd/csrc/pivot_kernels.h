@@ -59,6 +59,7 @@ struct RefineArgs {
   float* S;
   long long ldS;
   int row_base;
+  int excl = 0;  // window excluded: every member's limit is its position - excl
 };
 
 // Decode scan: for each sequence b, qr query rows (rows b*qr .. b*qr+qr-1 of
@@ -80,6 +81,7 @@ struct DecScanArgs {
   long long ldS;
   uint32_t* hist;
   int B;
+  int excl = 0;  // window excluded: every row's limit moves down by excl
 };
 
 // Top-m of decode score rows with precomputed first-digit histograms: `parts`
@@ -101,6 +103,7 @@ struct DecSelectArgs {
   int32_t* ccount;
   int32_t* out;
   long long ldo;
+  int excl = 0;  // window excluded: row lengths shrink by excl
 };
 
 // Row-length rules of the top-m selection.
@@ -125,6 +128,7 @@ struct TopkArgs {
   const int32_t* cache_len;
   const int32_t* map;  // kLenRefine: candidate lists
   int ldmap, map_grp_begin;
+  int excl = 0;        // kLenRefine / kLenCache / kLenDecodeDense: limits move down by excl
 };
 
 // Reuse: member rows [row_begin, row_end) receive their group's proxy top-k
@@ -137,6 +141,23 @@ struct BroadcastArgs {
   int decode, g, Lmax;
   const int32_t* cache_len;
   int row_begin, row_end;
+  long long ldo = 0;  // output row stride (0: topk)
+  int excl = 0;       // window excluded: member t keeps entries <= t - excl
+};
+
+// Sliding window added in place to selected rows: row i of out (stride ldo)
+// holds its selection in the first topk entries (ascending, -1 padded); the
+// row becomes the selection's entries below the window, then the window
+// max(0, t-W+1)..t, then -1 up to topk + W entries.  Row i's position t:
+// prefill row_begin + i; decode cache_len[b] - g + i % g for row i = b*g + i%g
+// (rows of an invalid sequence stay -1).
+struct WindowArgs {
+  int32_t* out;
+  long long ldo;
+  int rows, topk, W;
+  int decode, g, Lmax;
+  const int32_t* cache_len;
+  int row_begin;
 };
 
 hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st);
@@ -148,6 +169,7 @@ hipError_t launch_broadcast(const BroadcastArgs& a, hipStream_t st);
 hipError_t launch_selftest_mfma(int32_t* out, hipStream_t st);
 hipError_t launch_decode_select(const DecSelectArgs& a, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
+hipError_t launch_window_union(const WindowArgs& a, hipStream_t st);
 
 constexpr int kDecChunk = 2048;      // keys per decode-scan work item
 constexpr int kSelectCap = 7680;     // keys a long-row selection stages in LDS

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
     r = rb + wid;
     active = r <= rlast;
     const int pos = active ? min(r * a.pos_mul + a.pos_add, a.pos_cap) : -1;
-    nvalid = active ? min(pos + 1, k1) : 0;
+    nvalid = active ? max(0, min(pos + 1, k1)) : 0;  // a row may see no key at all
     srow_index = active ? r - a.row_begin : 0;
     krs = make_rsrc(a.k + (size_t)k0 * KT::ROW, (uint32_t)(k1 - k0) * KT::ROW);
     crs = krs;
@@ -236,14 +236,14 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
     if (a.kind == 0) {
       row0 = j * a.g;
       nmem = min(a.g, a.L - row0);
-      ncand = min(a.m, row0 + nmem);  // min(m, e_j + 1)
+      ncand = min(a.m, max(0, row0 + nmem - a.excl));  // min(m, e_j + 1 - excl)
       nkeys = a.L;
     } else {
       const int nb = a.cache_len[j];
       if (nb < a.g || nb > a.Lmax) return;
       row0 = j * a.g;
       nmem = a.g;
-      ncand = min(a.m, nb);
+      ncand = min(a.m, max(0, nb - a.excl));
       nkeys = nb;
       keybase = (size_t)j * a.Lmax;
     }
@@ -489,7 +489,7 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
         const size_t rowi = (size_t)b * a.qr + ri;
         q[i].load(a.q + rowi * a.H * ROW, a.w + rowi * a.H, a.H, lane);
         if constexpr (DT == kFP8) qs[i] = a.q_scale[rowi];
-        pos[i] = a.qr == 1 ? nb - 1 : nb - a.g + ri;
+        pos[i] = (a.qr == 1 ? nb - 1 : nb - a.g + ri) - a.excl;
       }
       // whole 16-byte pieces (the row stride is a multiple of 64 keys): the
       // up-to-3 scores past the causal limit that this lets through are unused

@@ -98,6 +98,7 @@ hipError_t launch_scan_dt(const ScanArgs& a_in, int D, hipStream_t st) {
   const int nrows = a.row_end - a.row_begin;
   const int rlast = a.row_end - 1;
   const int lim = min(rlast * a.pos_mul + a.pos_add, a.pos_cap) + 1;
+  if (nrows <= 0 || lim <= 0) return hipSuccess;  // no row sees any key
   dim3 grid((lim + a.kc - 1) / a.kc, (nrows + kScanRows - 1) / kScanRows);
   auto f = [&]<int D_, int HB_>() { scan_one<DT, D_, HB_>(a, grid, st); };
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;

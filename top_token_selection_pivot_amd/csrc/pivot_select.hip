@@ -231,11 +231,11 @@ __device__ inline int row_length(const TopkArgs& a, int R, const int32_t** list)
       return min(R * a.pos_mul + a.pos_add, a.pos_cap) + 1;
     case kLenCache: {
       const int nb = a.cache_len[R];
-      return (nb < a.g || nb > a.Lmax) ? 0 : nb;
+      return (nb < a.g || nb > a.Lmax) ? 0 : max(0, nb - a.excl);
     }
     case kLenDecodeDense: {
       const int b = R / a.g, i = R % a.g, nb = a.cache_len[b];
-      return (nb < a.g || nb > a.Lmax) ? 0 : nb - a.g + i + 1;
+      return (nb < a.g || nb > a.Lmax) ? 0 : max(0, nb - a.g + i + 1 - a.excl);
     }
     default: {  // kLenRefine
       int j, t;
@@ -243,10 +243,10 @@ __device__ inline int row_length(const TopkArgs& a, int R, const int32_t** list)
         j = R / a.g;
         const int nb = a.cache_len[j];
         if (nb < a.g || nb > a.Lmax) return 0;
-        t = nb - a.g + R % a.g;
+        t = nb - a.g + R % a.g - a.excl;
       } else {
         j = R / a.g;
-        t = R;
+        t = R - a.excl;
       }
       *list = a.map + (size_t)(j - a.map_grp_begin) * a.ldmap;
       return ref_count(*list, a.ldmap, t);
@@ -262,9 +262,9 @@ __device__ inline int refine_row_list(const TopkArgs& a, int R, const int32_t** 
   if (a.decode) {
     const int nb = a.cache_len[j];
     if (nb < a.g || nb > a.Lmax) return 0;
-    *t = nb - a.g + R % a.g;
+    *t = nb - a.g + R % a.g - a.excl;
   } else {
-    *t = R;
+    *t = R - a.excl;
   }
   *list = a.map + (size_t)(j - a.map_grp_begin) * a.ldmap;
   return 0;
@@ -815,10 +815,10 @@ constexpr int kGatherThreads = 256;
 __device__ inline int decode_row_length(const DecSelectArgs& a, int i) {
   if (a.kind == kLenCache) {
     const int nb = a.cache_len[i];
-    return (nb < a.g || nb > a.Lmax) ? 0 : nb;
+    return (nb < a.g || nb > a.Lmax) ? 0 : max(0, nb - a.excl);
   }
   const int b = i / a.g, nb = a.cache_len[b];
-  return (nb < a.g || nb > a.Lmax) ? 0 : nb - a.g + i % a.g + 1;
+  return (nb < a.g || nb > a.Lmax) ? 0 : max(0, nb - a.g + i % a.g + 1 - a.excl);
 }
 
 // Threshold bin of the rem-th largest key from a global 4096-bin histogram,
@@ -1001,13 +1001,13 @@ __global__ __launch_bounds__(256) void broadcast_kernel(BroadcastArgs a) {
   if (a.decode) {
     j = R / a.g;
     const int nb = a.cache_len[j];
-    t = (nb < a.g || nb > a.Lmax) ? -1 : nb - a.g + R % a.g;
+    t = (nb < a.g || nb > a.Lmax) ? -1 : nb - a.g + R % a.g - a.excl;
   } else {
     j = R / a.g;
-    t = R;
+    t = R - a.excl;
   }
   const int32_t* p = a.ptop + (size_t)(j - a.grp_begin) * a.ldp;
-  int32_t* out = a.out + (size_t)blockIdx.x * a.topk;
+  int32_t* out = a.out + (size_t)blockIdx.x * (a.ldo ? a.ldo : a.topk);
   for (int s = threadIdx.x; s < a.topk; s += 256) {
     const int v = p[s];
     out[s] = (v >= 0 && v <= t) ? v : -1;
@@ -1018,6 +1018,52 @@ hipError_t launch_broadcast(const BroadcastArgs& a, hipStream_t st) {
   const int n = a.row_end - a.row_begin;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(broadcast_kernel, dim3(n), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Sliding window added to the selection (tutorial "Sparse Attention의
+// Indexer", section on combining the recent window with the selected
+// positions, Figure 3): the window of size W at position t is
+// max(0, t-W+1)..t, and each position of the union is read once.  The
+// selection is ascending, so its entries below the window form a prefix; the
+// row keeps that prefix and continues with the window, in place.  With the
+// window excluded from the candidates the selection lies entirely below the
+// window and the same step appends it.
+// ---------------------------------------------------------------------------
+constexpr int kWindowThreads = 256;
+
+__global__ __launch_bounds__(kWindowThreads) void window_union_kernel(WindowArgs a) {
+  __shared__ uint32_t scratch[kWindowThreads / kWave + 1];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  int32_t* row = a.out + (long long)i * a.ldo;
+  int t;
+  if (a.decode) {
+    const int nb = a.cache_len[i / a.g];
+    t = (nb < a.g || nb > a.Lmax) ? -1 : nb - a.g + i % a.g;
+  } else {
+    t = a.row_begin + i;
+  }
+  const int lo = max(0, t - a.W + 1);
+  // entries of the selection below the window (the selection's -1 tail and
+  // its entries inside the window are not counted)
+  uint32_t c = 0;
+  for (int e = tid; e < a.topk; e += kWindowThreads) {
+    const int v = row[e];
+    c += (v >= 0 && v < lo) ? 1u : 0u;
+  }
+  uint32_t keep;
+  block_exclusive_sum<kWindowThreads>(c, scratch, &keep);  // ends with a barrier: reads done
+  const int nwin = t < 0 ? 0 : t - lo + 1;
+  for (int e = (int)keep + tid; e < a.topk + a.W; e += kWindowThreads) {
+    const int u = e - (int)keep;
+    row[e] = u < nwin ? lo + u : -1;
+  }
+}
+
+hipError_t launch_window_union(const WindowArgs& a, hipStream_t st) {
+  if (a.rows <= 0 || a.W <= 0) return hipSuccess;
+  hipLaunchKernelGGL(window_union_kernel, dim3(a.rows), dim3(kWindowThreads), 0, st, a);
   return hipGetLastError();
 }
 
