@@ -346,6 +346,28 @@ def main():
         sweep["reuse_g8"] = {"ms_per_step": s * 1e3, "queries_per_s": L / s,
                              "speedup_vs_dense": sec_d / s}
         extras["g_sweep"] = sweep
+        # sliding window added to the selection (both designs), Refine g=8
+        W = 128
+        out_w = torch.empty((L, topk + W), dtype=torch.int32, device="cuda")
+        win = {"window": W}
+        for wm in ("shared", "excluded"):
+            f = lambda: pv.indexer(d["q"], d["w"], d["k"], g=g, topk=topk, C=C, mode="refine",
+                                   out=out_w, workspace=ws, window=W, window_mode=wm)
+            s = time_steps(f, 3, 1, torch)
+            pv.profile_enable(True)
+            pv.profile_read()
+            f()
+            torch.cuda.synchronize()
+            prof = pv.profile_read()
+            pv.profile_enable(False)
+            wms, wn = prof["window"]
+            # the union reads each row's selection (topk entries) and writes
+            # the rest of the row: (topk + topk + W) * 4 bytes per row at most
+            ub = L * (2 * topk + W) * 4
+            win[wm] = {"ms_per_step": s * 1e3, "queries_per_s": L / s,
+                       "union_kernel_ms": wms / max(1, wn), "union_kernel_GBs": ub / (wms / max(1, wn)) / 1e6}
+        extras["window_refine_g8"] = win
+        del out_w
         log(f"dense {sec_d*1e3:.1f} ms; speedup {sec_d/sec:.2f}x; overlap {ov.mean():.4f}")
         del d, ws, out
         torch.cuda.empty_cache()

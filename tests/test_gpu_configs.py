@@ -141,3 +141,69 @@ def test_decode_mtp_b32():
                     sc = oracle.score_pairs(v, np.full(len(pool), i), pool)
                     check_band(r, pool, sc, 2048, EPS_FP8, f"refine seq {b} member {i}")
         print(f"decode {mode}: ok", flush=True)
+
+
+def _check_window_rows(rows, positions, W, topk, excluded):
+    """Rows with a sliding window: the selection's entries below the window,
+    then every position of the window, then -1; with the window excluded the
+    selection holds min(topk, t-W+1) entries (dense and Refine)."""
+    sel = []
+    for r, t in zip(rows, positions):
+        lo = max(0, int(t) - W + 1)
+        valid = r[r >= 0]
+        assert np.all(np.diff(valid) > 0) and np.all(r[len(valid):] == -1), t
+        s = valid[valid < lo]
+        assert valid[len(s):].tolist() == list(range(lo, int(t) + 1)), t
+        if excluded:
+            assert len(s) == min(topk, max(0, int(t) - W + 1)), t
+        sel.append(np.concatenate([s, np.full(topk - len(s), -1)]))
+    return np.array(sel)
+
+
+def test_window_16k_and_decode():
+    print("case: window 128 (shared, excluded) at the 16K prefill and the B=32 decode step",
+          flush=True)
+    W, topk = 128, 2048
+    inp = synth.make("dsa_prefill_16k")
+    d = to_device(inp)
+    v = oracle.View.of(inp)
+    L = inp.L
+    kw = dict(g=8, topk=topk, C=4096, mode="refine")
+    plain = pv.indexer(d["q"], d["w"], d["k"], **kw).cpu().numpy()
+    shared = pv.indexer(d["q"], d["w"], d["k"], window=W, window_mode="shared", **kw).cpu().numpy()
+    # the shared window leaves the selection as it is: exactly the union
+    assert np.array_equal(shared, oracle.window_union(plain, np.arange(L), W))
+    excl = pv.indexer(d["q"], d["w"], d["k"], window=W, window_mode="excluded", **kw).cpu().numpy()
+    _check_window_rows(excl, np.arange(L), W, topk, True)
+    dx = pv.indexer(d["q"], d["w"], d["k"], g=1, topk=topk, C=topk, mode="dense", window=W,
+                    window_mode="excluded").cpu().numpy()
+    rows = [0, 127, 128, 2175, 9000, 16383]
+    sel = _check_window_rows(dx[rows], rows, W, topk, True)
+    for r, t in zip(sel, rows):
+        n = max(0, t - W + 1)
+        sc = oracle.score_row(v, t, n) if n else np.zeros(0)
+        check_band(r, np.arange(n), sc, topk, EPS_BF16, f"dense window-excluded row {t}")
+
+    dec = synth.make("decode_mtp_b32")
+    d = to_device(dec)
+    pos = (dec.cache_len[:, None] - 2 + np.arange(2)[None, :]).reshape(-1)
+    dkw = dict(topk=topk, C=4096, q_scale=d["q_scale"], k_scale=d["k_scale"])
+    for mode in ("refine", "dense"):
+        plain = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], mode=mode, **dkw)
+        shared = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], mode=mode, window=W,
+                                   window_mode="shared", **dkw)
+        plain = plain.cpu().numpy().reshape(-1, topk)
+        assert np.array_equal(shared.cpu().numpy().reshape(-1, topk + W),
+                              oracle.window_union(plain, pos, W))
+        ex = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], mode=mode, window=W,
+                               window_mode="excluded", **dkw).cpu().numpy().reshape(-1, topk + W)
+        sel = _check_window_rows(ex, pos, W, topk, True)
+        if mode == "dense":
+            for b in (0, 31):
+                vb = oracle.decode_view(dec, b)
+                for i in range(2):
+                    t = int(pos[2 * b + i])
+                    n = t - W + 1
+                    sc = oracle.score_row(vb, i, n)
+                    check_band(sel[2 * b + i], np.arange(n), sc, topk, EPS_FP8,
+                               f"decode dense window-excluded seq {b}")
