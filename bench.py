@@ -119,18 +119,34 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
     key_bytes = float(dec.cache_len.astype(np.int64).sum()) * (D + 4)
     scan_ms_d = dprof["decode_scan"][0] / nd_prof
     dense_dsec = time_steps(lambda: dstep("dense"), max(1, nd_steps // 2), 5, torch)
+    # a deeper multi-token-prediction group: four queries per sequence, same
+    # cache lengths and distributions
+    del dd, dws, dout
+    torch.cuda.empty_cache()
+    dec4 = synth.make("decode_mtp_b32", g=4)
+    dd4 = upload(dec4, torch)
+    ws4 = torch.empty(pv.decode_workspace_size(B, Lmax, H, D, 4, topk, C, "refine", 1),
+                      dtype=torch.uint8, device="cuda")
+    out4 = torch.empty((B, 4, topk), dtype=torch.int32, device="cuda")
+    g4_sec = time_steps(lambda: pv.indexer_decode(dd4["q"], dd4["w"], dd4["k"], dd4["cache_len"],
+                                                  topk=topk, C=C, mode="refine",
+                                                  q_scale=dd4["q_scale"], k_scale=dd4["k_scale"],
+                                                  out=out4, workspace=ws4),
+                        max(1, nd_steps // 2), 5, torch)
+    del dd4, ws4, out4
     res = {
         "workload": "decode_mtp_b32 (B=32, g=2, fp8, cache 32K-128K)",
         "us_per_step": dsec * 1e6,
         "dense_us_per_step": dense_dsec * 1e6,
+        "refine_g4_us_per_step": g4_sec * 1e6,
         "key_stream_bytes": key_bytes,
         "decode_scan_us": scan_ms_d * 1e3,
         "decode_scan_hbm_GBs": key_bytes / (scan_ms_d / 1e3) / 1e9,
         "decode_scan_hbm_frac": key_bytes / (scan_ms_d / 1e3) / 1e9 / HBM_PEAK_GBS,
         "kernels_us": {k: v[0] / nd_prof * 1e3 for k, v in dprof.items() if v[1]},
     }
-    log(f"decode {dsec*1e6:.1f} us/step; scan {key_bytes/(scan_ms_d/1e3)/1e9:.0f} GB/s")
-    del dd, dws, dout
+    log(f"decode {dsec*1e6:.1f} us/step; scan {key_bytes/(scan_ms_d/1e3)/1e9:.0f} GB/s; "
+        f"g=4 {g4_sec*1e6:.1f} us/step")
     torch.cuda.empty_cache()
     return res
 

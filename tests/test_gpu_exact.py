@@ -336,3 +336,25 @@ def test_decode_fp8_exact_dense():
     for b in range(4):
         ref, _, _ = oracle.decode_seq(dec, b, 50, 50, "dense")
         assert np.array_equal(out[b], ref), b
+
+
+@pytest.mark.parametrize("g", [3, 4, 8])
+@pytest.mark.parametrize("mode", ["dense", "reuse", "refine"])
+def test_decode_deeper_mtp_groups(g, mode):
+    # more than two tokens per multi-token-prediction step: the group is the g
+    # queries decoded together, the proxy their mean over the whole cache
+    print(f"case: decode MTP group g={g} B=10 H=16 D=64 bf16 {mode}", flush=True)
+    rng = np.random.default_rng(g)
+    lens = [int(x) for x in rng.integers(g, 2500, 10)]
+    lens[2], lens[6] = g, g - 1  # the smallest valid cache and an invalid one
+    dec = _decode_inputs(10, lens, g=g, H=16, D=64, Lmax=2500, seed=60 + g)
+    d = to_device(dec)
+    out = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=40, C=120,
+                            mode=mode).cpu().numpy()
+    assert out.shape == (10, g, 40)
+    for b in range(10):
+        if lens[b] < g:
+            assert np.all(out[b] == -1), b
+            continue
+        ref, _, _ = oracle.decode_seq(dec, b, 40, 120, mode)
+        assert np.array_equal(out[b], ref), b
