@@ -74,6 +74,9 @@ def lib():
         L.orc_prefill_groups_ex.argtypes = [C.POINTER(_View), C.c_int, C.c_int, C.c_int, C.c_int,
                                             C.c_int, C.c_int, i32p, C.c_int, i32p, C.c_void_p]
         L.orc_window_union.argtypes = [i32p, C.c_int, C.c_int, C.c_int, i32p]
+        u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+        L.orc_sparse_attention.argtypes = [u16p, u16p, u16p, i32p] + [C.c_int] * 6 + [
+            C.c_long, C.c_int, C.c_double, f64p]
         L.orc_score_row.argtypes = [C.POINTER(_View), C.c_int, C.c_int, f64p]
         L.orc_score_pairs.argtypes = [C.POINTER(_View), i32p, i32p, C.c_int, f64p]
         _lib = L
@@ -262,3 +265,27 @@ def decode_seq(dec, b: int, topk_: int, C_: int, mode):
     shared scan covers the whole cache [0, n_b)."""
     n = int(dec.cache_len[b])
     return group(decode_view(dec, b), 0, n - dec.g, dec.g, topk_, C_, mode)
+
+
+def sparse_attention(q, k, v, idx, rows_per_seq=None, seq_len=None, scale=None):
+    """Sparse main attention over the selected positions ([TUT] text after
+    Figure 1), multi-query layout, in double.  q [R,Hq,d] bf16 codes; k [N,d] or
+    [B,S,d] and v [N,dv] or [B,S,dv] bf16 codes; idx [R,nidx].  Row r reads
+    sequence r // rows_per_seq (default: one sequence).  Returns [R,Hq,dv]."""
+    q = np.ascontiguousarray(q, np.uint16)
+    idx = np.ascontiguousarray(idx, np.int32)
+    R, Hq, d = q.shape
+    dv = v.shape[-1]
+    if k.ndim == 2:
+        stride, nkeys = 0, k.shape[0]
+        rows_per_seq = R if rows_per_seq is None else rows_per_seq
+    else:
+        stride, nkeys = k.shape[1], k.shape[1]
+    k = np.ascontiguousarray(k, np.uint16).reshape(-1, d)
+    v = np.ascontiguousarray(v, np.uint16).reshape(-1, dv)
+    seq_len = nkeys if seq_len is None else seq_len
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    out = np.empty((R, Hq, dv), np.float64)
+    lib().orc_sparse_attention(q, k, v, idx, R, Hq, d, dv, idx.shape[1], rows_per_seq, stride,
+                               seq_len, float(scale), out)
+    return out

@@ -437,3 +437,53 @@ void orc_window_union(const int32_t* sel, int k, int t, int W, int32_t* out) {
   for (; c < k + W; ++c) out[c] = -1;
   free(all);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sparse main attention over the selected positions ([TUT] text after      */
+/* Figure 1: the main query scores the main keys at the selected positions  */
+/* only, and the values there are combined with softmax weights over those  */
+/* positions; the indexer scores are not the weights).  Reading: standard   */
+/* scaled dot-product attention, one key and one value row per position     */
+/* shared by all query heads (multi-query layout).  Computed in double.     */
+/* q [R][Hq][d] bf16 codes; k [nseq][seq_stride][d], v [nseq][seq_stride][dv] */
+/* bf16 codes; row r belongs to sequence r / rows_per_seq; idx [R][nidx]    */
+/* positions, entries outside [0, seq_len) are skipped; out [R][Hq][dv].    */
+/* A row with no selected position gets zeros.                              */
+/* ------------------------------------------------------------------------ */
+
+void orc_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* idx, int R, int Hq, int d, int dv, int nidx,
+                          int rows_per_seq, long seq_stride, int seq_len, double scale,
+                          double* out) {
+  double* sc = (double*)malloc(sizeof(double) * (size_t)(nidx > 0 ? nidx : 1));
+  for (int r = 0; r < R; ++r) {
+    const long base = (long)(r / rows_per_seq) * seq_stride;
+    const int32_t* sel = idx + (long)r * nidx;
+    for (int h = 0; h < Hq; ++h) {
+      double* o = out + ((long)r * Hq + h) * dv;
+      for (int c = 0; c < dv; ++c) o[c] = 0.0;
+      const uint16_t* qh = q + ((long)r * Hq + h) * d;
+      double mx = -INFINITY;
+      for (int i = 0; i < nidx; ++i) {
+        sc[i] = -INFINITY;
+        if (sel[i] < 0 || sel[i] >= seq_len) continue;
+        const uint16_t* kr = k + (base + sel[i]) * d;
+        double dot = 0.0;
+        for (int e = 0; e < d; ++e) dot += orc_bf16_value(qh[e]) * orc_bf16_value(kr[e]);
+        sc[i] = dot * scale;
+        if (sc[i] > mx) mx = sc[i];
+      }
+      if (mx == -INFINITY) continue; /* nothing selected */
+      double den = 0.0;
+      for (int i = 0; i < nidx; ++i) {
+        if (sc[i] == -INFINITY) continue;
+        double p = exp(sc[i] - mx);
+        den += p;
+        const uint16_t* vr = v + (base + sel[i]) * dv;
+        for (int c = 0; c < dv; ++c) o[c] += p * orc_bf16_value(vr[c]);
+      }
+      for (int c = 0; c < dv; ++c) o[c] /= den;
+    }
+  }
+  free(sc);
+}

@@ -107,6 +107,17 @@ void orc_prefill_groups_ex(const orc_view* v, int L, int g, int topk, int C, int
  * position once, -1 padded to k + W entries. */
 void orc_window_union(const int32_t* sel, int k, int t, int W, int32_t* out);
 
+/* Sparse main attention over the selected positions (multi-query layout,
+ * computed in double): out[r][h] = sum over the valid selected s of
+ * softmax_s(scale * q[r][h] . k_s) v_s.  q [R][Hq][d], k [.][d], v [.][dv] are
+ * bf16 codes; row r reads sequence r / rows_per_seq, whose rows start at
+ * (r / rows_per_seq) * seq_stride; idx [R][nidx] entries outside [0, seq_len)
+ * are skipped; a row with none gets zeros.  out [R][Hq][dv]. */
+void orc_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* idx, int R, int Hq, int d, int dv, int nidx,
+                          int rows_per_seq, long seq_stride, int seq_len, double scale,
+                          double* out);
+
 /* Scores of the query row `row` of the view against keys [0, n). */
 void orc_score_row(const orc_view* v, int row, int n, double* out);
 
