@@ -156,6 +156,34 @@ int pivot_indexer_decode_window(const void* q, const float* q_scale, const float
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Sparse main attention over the selected positions (tutorial "Sparse
+ * Attention의 Indexer", text after Figure 1): the main query of a row scores
+ * the main keys at the positions the indexer selected and combines the values
+ * there with softmax weights over those positions only:
+ *     out[r][h] = sum_s softmax_s(scale * q[r][h] . k_s) v_s,  s in idx[r].
+ * Multi-query layout: one key row and one value row per position, shared by
+ * the Hq query heads.  bf16 codes; d = dv = 128; Hq in {32, 64}.
+ *
+ *   q    [R][Hq][d]       out [R][Hq][dv] float (16-byte aligned)
+ *   k    key rows of d codes, v value rows of dv codes: row r reads sequence
+ *        r / rows_per_seq, whose rows start at row (r / rows_per_seq) *
+ *        seq_stride (one sequence: rows_per_seq = R, seq_stride unused)
+ *   idx  [R][nidx] int32 positions in the row's sequence (an indexer output,
+ *        e.g. pivot_indexer's rows); entries outside [0, seq_len) are skipped
+ *        and a row with none gets zeros
+ *   scale  > 0, applied to every dot product (usually 1/sqrt(d))
+ * Scores and sums are binary32; the softmax weights enter the value product
+ * as two bf16 terms, so the result is close to binary32 accuracy.  Few rows
+ * split their slots over several waves and need a workspace of
+ * pivot_sparse_attention_workspace_size bytes (0: none needed).
+ * ------------------------------------------------------------------------- */
+size_t pivot_sparse_attention_workspace_size(int R, int Hq, int dv, int nidx);
+int pivot_sparse_attention(const void* q, const void* k, const void* v, const int32_t* idx, int R,
+                           int Hq, int d, int dv, int nidx, int rows_per_seq, long long seq_stride,
+                           int seq_len, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Single steps of the prefill path, for step-level checks.
  *
  * pivot_proxy_mean: the proxy of every group (arXiv:2607.24593 abstract: one
@@ -204,7 +232,8 @@ enum {
   PIVOT_K_BROADCAST = 5,    /* Reuse broadcast */
   PIVOT_K_DECODE_SCAN = 6,  /* decode key-cache scan */
   PIVOT_K_WINDOW = 7,       /* sliding-window union */
-  PIVOT_K_COUNT = 8
+  PIVOT_K_ATTENTION = 8,    /* sparse main attention (and its chunk merge) */
+  PIVOT_K_COUNT = 9
 };
 int pivot_profile_enable(int on);
 int pivot_profile_read(double* ms, long long* launches, int n);

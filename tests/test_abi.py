@@ -140,3 +140,24 @@ def test_window_validation(lib):
         assert f(1 << 30, 1) == ERR_PARAM
         assert f(3, 0, out=None) == ERR_NULL
         assert f(3, 1, wsb=100) == ERR_WORKSPACE  # valid window: fails only on the workspace
+
+
+def test_sparse_attention_validation(lib):
+    def f(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, idx=FAKE, R=64, Hq=64, d=128, dv=128, nidx=2048, rps=2,
+                 stride=131072, seq_len=131072, scale=0.088, out=FAKE, ws=FAKE, wsb=100)
+        a.update(kw)
+        return lib.pivot_sparse_attention(a["q"], a["k"], a["v"], a["idx"], a["R"], a["Hq"], a["d"],
+                                          a["dv"], a["nidx"], a["rps"], a["stride"], a["seq_len"],
+                                          a["scale"], a["out"], a["ws"], a["wsb"], None)
+    assert f(q=None) == ERR_NULL
+    assert f(Hq=48) == ERR_SHAPE
+    assert f(d=64) == ERR_SHAPE
+    assert f(R=0) == ERR_SHAPE
+    assert f(rps=0) == ERR_PARAM
+    assert f(stride=100) == ERR_PARAM          # sequences would overlap
+    assert f(scale=0.0) == ERR_PARAM
+    assert f(out=FAKE + 4) == ERR_ALIGN
+    assert f() == ERR_WORKSPACE                 # 64 rows: chunks merged through the workspace
+    assert lib.pivot_sparse_attention_workspace_size(64, 64, 128, 2048) > 0
+    assert lib.pivot_sparse_attention_workspace_size(4096, 64, 128, 2048) == 0  # one chunk per row

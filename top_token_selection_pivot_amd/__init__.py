@@ -78,6 +78,11 @@ def load():
     L.pivot_indexer_window.argtypes = [vp, fp, fp, vp, fp] + [i] * 10 + [ip, vp, sz, vp]
     L.pivot_indexer_decode_window.restype = i
     L.pivot_indexer_decode_window.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 11 + [ip, vp, sz, vp]
+    L.pivot_sparse_attention_workspace_size.restype = sz
+    L.pivot_sparse_attention_workspace_size.argtypes = [i] * 4
+    L.pivot_sparse_attention.restype = i
+    L.pivot_sparse_attention.argtypes = [vp, vp, vp, ip] + [i] * 6 + [C.c_longlong, i, C.c_float,
+                                                                      fp, vp, sz, vp]
     L.pivot_decode_candidates.restype = i
     L.pivot_decode_candidates.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, vp, sz, vp]
     L.pivot_profile_enable.restype = i
@@ -272,6 +277,41 @@ def decode_candidates(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="
     return cand
 
 
+def sparse_attention(q, k, v, idx, *, rows_per_seq: Optional[int] = None, seq_len=None,
+                     scale=None, out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Sparse main attention over the selected positions (pivot_sparse_attention).
+
+    q [R,Hq,d] bf16; k [N,d] and v [N,dv] bf16 (one sequence) or [B,S,d] and
+    [B,S,dv] (row r reads sequence r // rows_per_seq); idx [R,nidx] int32
+    positions (-1 and out-of-range entries are skipped).  Returns float32
+    [R,Hq,dv]."""
+    import math
+    L = load()
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    idx = _dev(idx, "idx", torch.int32)
+    R, Hq, d = q.shape
+    dv = v.shape[-1]
+    if k.dim() == 2:
+        stride, nkeys = 0, k.shape[0]
+        rows_per_seq = R if rows_per_seq is None else rows_per_seq
+    else:
+        stride, nkeys = k.shape[1], k.shape[1]
+        if rows_per_seq is None:
+            raise ValueError("rows_per_seq is needed with per-sequence k/v")
+    seq_len = nkeys if seq_len is None else seq_len
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nidx = idx.shape[1]
+    if out is None:
+        out = torch.empty((R, Hq, dv), dtype=torch.float32, device=q.device)
+    need = L.pivot_sparse_attention_workspace_size(R, Hq, dv, nidx)
+    ws = _workspace(need, q.device, workspace) if need else None
+    _check(L.pivot_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), R, Hq, d, dv, nidx,
+                                    rows_per_seq, stride, seq_len, float(scale), _ptr(out),
+                                    _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+    return out
+
+
 def selftest_mfma_layout(device="cuda") -> torch.Tensor:
     """[3, 2, 64, 16] int32: row / column / pairing probes for bf16 and fp8 tiles."""
     L = load()
@@ -281,7 +321,7 @@ def selftest_mfma_layout(device="cuda") -> torch.Tensor:
 
 
 KERNEL_CLASSES = ("proxy_mean", "scan", "select", "refine_score", "member_select", "broadcast",
-                  "decode_scan", "window")
+                  "decode_scan", "window", "attention")
 
 
 def profile_enable(on: bool = True) -> None:

@@ -566,6 +566,68 @@ int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,
                     dtype, nullptr, cand, workspace, workspace_bytes, stream);
 }
 
+// Sparse main attention: chunks per row.  Many rows: one chunk each (no
+// merge); few rows: chunks of kSAttnChunk slots so that about 1024 waves run.
+constexpr int kSAttnChunk = 128;
+
+static void sattn_plan(int R, int nidx, int* chunk, int* nch) {
+  const int slots = (nidx + 31) / 32 * 32;
+  if ((long long)R >= 1024 || nidx <= kSAttnChunk) {
+    *chunk = std::max(32, slots);
+    *nch = 1;
+    return;
+  }
+  const int want = std::max(1, std::min((1024 + R - 1) / R, (slots + kSAttnChunk - 1) / kSAttnChunk));
+  *chunk = (slots / want + 31) / 32 * 32;
+  *nch = (nidx + *chunk - 1) / *chunk;
+}
+
+size_t pivot_sparse_attention_workspace_size(int R, int Hq, int dv, int nidx) {
+  if (R < 1 || Hq < 1 || dv < 1 || nidx < 1) return 0;
+  int chunk, nch;
+  sattn_plan(R, nidx, &chunk, &nch);
+  if (nch == 1) return 0;
+  return align_up((size_t)R * nch * Hq * dv * 4) + align_up((size_t)R * nch * 2 * Hq * 4);
+}
+
+int pivot_sparse_attention(const void* q, const void* k, const void* v, const int32_t* idx, int R,
+                           int Hq, int d, int dv, int nidx, int rows_per_seq, long long seq_stride,
+                           int seq_len, float scale, float* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !idx || !out) return fail(PIVOT_ERR_NULL, "q, k, v, idx and out must be non-NULL");
+  if (R < 1 || nidx < 1) return fail(PIVOT_ERR_SHAPE, "R=%d and nidx=%d must be >= 1", R, nidx);
+  if (!sattn_shape_supported(Hq, d, dv))
+    return fail(PIVOT_ERR_SHAPE, "sparse attention supports d = dv = 128 and Hq in {32, 64} (got %d, %d, %d)", d,
+                dv, Hq);
+  if (rows_per_seq < 1 || seq_len < 0 || seq_stride < 0)
+    return fail(PIVOT_ERR_PARAM, "rows_per_seq=%d must be >= 1, seq_len=%d and seq_stride=%lld >= 0", rows_per_seq,
+                seq_len, seq_stride);
+  if ((R - 1) / rows_per_seq > 0 && seq_stride < seq_len)
+    return fail(PIVOT_ERR_PARAM, "seq_stride=%lld is below seq_len=%d with several sequences", seq_stride, seq_len);
+  if ((long long)seq_len * std::max(d, dv) * 2 >= (1ll << 32))
+    return fail(PIVOT_ERR_SHAPE, "one sequence's key or value rows must stay below 4 GiB");
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PIVOT_ERR_PARAM, "scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(idx, 4))
+    return fail(PIVOT_ERR_ALIGN, "q, k, v and out must be 16-byte aligned, idx 4-byte aligned");
+  int chunk, nch;
+  sattn_plan(R, nidx, &chunk, &nch);
+  const size_t need = pivot_sparse_attention_workspace_size(R, Hq, dv, nidx);
+  if (need > 0) {
+    if (!workspace) return fail(PIVOT_ERR_NULL, "workspace must be non-NULL (%zu bytes)", need);
+    if (!aligned(workspace, kAlign)) return fail(PIVOT_ERR_ALIGN, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", workspace_bytes, need);
+  }
+  uint8_t* ws = (uint8_t*)workspace;
+  SAttnArgs a{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, R, Hq, nidx, rows_per_seq,
+              seq_stride, seq_len, scale, chunk, nch, out,
+              need ? (float*)ws : nullptr,
+              need ? (float*)(ws + align_up((size_t)R * nch * Hq * dv * 4)) : nullptr};
+  hipStream_t s = (hipStream_t)stream;
+  PIVOT_LAUNCH_K(PIVOT_K_ATTENTION, s, launch_sparse_attention(a, s), "sparse attention");
+  return PIVOT_OK;
+}
+
 int pivot_profile_enable(int on) {
   g_prof_on.store(on != 0);
   return PIVOT_OK;

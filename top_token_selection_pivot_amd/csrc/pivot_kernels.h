@@ -160,6 +160,29 @@ struct WindowArgs {
   int row_begin;
 };
 
+// Sparse main attention (multi-query, bf16 codes, D = DV = 128, Hq in {32, 64}):
+// row r reads sequence r / rows_per_seq, whose key and value rows start at row
+// (r / rows_per_seq) * seq_stride of k and v; idx [R][nidx] entries outside
+// [0, seq_len) are skipped.  Each of the nch chunks of a row covers `chunk`
+// slots (a multiple of 32); with nch == 1 the output [R][Hq][DV] is written
+// directly, otherwise part_o [R][nch][Hq][DV] and part_ml [R][nch][2][Hq]
+// (running maximum, then sum) are merged by a second kernel.
+struct SAttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  int R, Hq, nidx;
+  int rows_per_seq;
+  long long seq_stride;
+  int seq_len;
+  float scale;
+  int chunk, nch;
+  float* out;
+  float* part_o;
+  float* part_ml;
+};
+
 hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_refine(const RefineArgs& a, int dtype, int D, hipStream_t st);
@@ -176,5 +199,7 @@ constexpr int kSelectCap = 7680;     // keys a long-row selection stages in LDS
 constexpr int kSelectBins1 = 4096;   // bins of the first radix digit (top 12 bits)
 
 bool score_shape_supported(int dtype, int D);
+bool sattn_shape_supported(int Hq, int d, int dv);
+hipError_t launch_sparse_attention(const SAttnArgs& a, hipStream_t st);
 
 }  // namespace pivot
