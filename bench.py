@@ -53,6 +53,8 @@ def parse():
                     help="first run 3 plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the MTP decode step (used under a profiler)")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="time only the sparse main attention after the indexer")
     return ap.parse_args()
 
 
@@ -147,6 +149,61 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
     }
     log(f"decode {dsec*1e6:.1f} us/step; scan {key_bytes/(scan_ms_d/1e3)/1e9:.0f} GB/s; "
         f"g=4 {g4_sec*1e6:.1f} us/step")
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_attention(torch, pv, synth):
+    """Sparse main attention after the indexer (multi-query, 64 heads,
+    d = dv = 128, bf16 keys and values): the B=32 decode step on the decode
+    workload's Refine rows, and the 16K prefill on its Refine rows.  Reports
+    time, the bytes of key and value rows the selected positions gather, and
+    the matrix-core work 2 * Hq * (d + dv) per selected position."""
+    Hq, d = 64, 128
+    res = {}
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    # decode: Refine rows of the decode workload
+    dec = synth.make("decode_mtp_b32")
+    dd = upload(dec, torch)
+    B, Lmax, g = dec.B, dec.Lmax, dec.g
+    rows = pv.indexer_decode(dd["q"], dd["w"], dd["k"], dd["cache_len"], topk=2048, C=4096,
+                             mode="refine", q_scale=dd["q_scale"], k_scale=dd["k_scale"])
+    del dd
+    idx = rows.reshape(B * g, 2048).contiguous()
+    kc = torch.randn((B, Lmax, d), generator=gen, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((B, Lmax, d), generator=gen, device="cuda").to(torch.bfloat16)
+    qa = torch.randn((B * g, Hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((B * g, Hq, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, pv.load().pivot_sparse_attention_workspace_size(B * g, Hq, d, 2048)),
+                     dtype=torch.uint8, device="cuda")
+    f = lambda: pv.sparse_attention(qa, kc, vc, idx, rows_per_seq=g, out=out, workspace=ws)
+    sec = time_steps(f, 50, 5, torch)
+    nsel = float((idx >= 0).sum().item())
+    gb = nsel * 2 * d * 2 + qa.numel() * 2 + out.numel() * 4
+    res["decode_b32"] = {"us_per_step": sec * 1e6, "selected_positions": nsel,
+                         "bytes": gb, "GBs": gb / sec / 1e9, "hbm_frac": gb / sec / 1e9 / HBM_PEAK_GBS}
+    del kc, vc, qa, out, ws, idx, rows
+    torch.cuda.empty_cache()
+    # prefill: Refine rows of the 16K workload
+    inp = synth.make("dsa_prefill_16k")
+    dp = upload(inp, torch)
+    L = inp.L
+    rows = pv.indexer(dp["q"], dp["w"], dp["k"], g=8, topk=2048, C=4096, mode="refine")
+    del dp
+    kp = torch.randn((L, d), generator=gen, device="cuda").to(torch.bfloat16)
+    vp = torch.randn((L, d), generator=gen, device="cuda").to(torch.bfloat16)
+    qp = torch.randn((L, Hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((L, Hq, d), dtype=torch.float32, device="cuda")
+    f = lambda: pv.sparse_attention(qp, kp, vp, rows, out=out)
+    sec = time_steps(f, 3, 1, torch)
+    nsel = float((rows >= 0).sum().item())
+    fl = 2.0 * Hq * 2 * d * nsel
+    res["prefill_16k"] = {"ms_per_call": sec * 1e3, "selected_positions": nsel,
+                          "TFLOPs": fl / sec / 1e12, "mfma_frac": fl / sec / 1e12 / BF16_PEAK_TFLOPS}
+    log(f"sparse attention: decode {res['decode_b32']['us_per_step']:.1f} us "
+        f"({res['decode_b32']['GBs']:.0f} GB/s), prefill 16K {sec*1e3:.2f} ms "
+        f"({fl/sec/1e12:.0f} TFLOP/s)")
+    del kp, vp, qp, out, rows
     torch.cuda.empty_cache()
     return res
 
@@ -249,6 +306,11 @@ def main():
                           "value": res["us_per_step"], "unit": "us/step", "n_gpus": 1,
                           "steps": args.steps, "higher_is_better": False, "decode": res}),
               flush=True)
+        return
+    if args.attention_only:
+        res = measure_attention(torch, pv, synth)
+        print(json.dumps({"metric": "sparse attention after the indexer", "n_gpus": 1,
+                          "sparse_attention": res}), flush=True)
         return
     L, H, D, g, topk, C = 131072, 64, 128, args.g, 2048, 4096
     log("generating the 128K prefill inputs")
@@ -389,6 +451,7 @@ def main():
         torch.cuda.empty_cache()
 
         extras["decode"] = measure_decode(torch, pv, synth, 200, 100)
+        extras["sparse_attention"] = measure_attention(torch, pv, synth)
         extras["pages_claims_context"] = ("up to 4x indexer speedup, about 3x for Refine, "
                                           "1.6x end-to-end on DeepSeek-V3.2/GLM-5.1; "
                                           "no hardware stated")

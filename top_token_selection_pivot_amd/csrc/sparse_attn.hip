@@ -80,26 +80,33 @@ __global__ __launch_bounds__(kWave) void sattn_kernel(SAttnArgs a) {
     l[nb] = 0.f;
   }
 
+  // the positions of the next tile are loaded one tile ahead
+  int pos_next = s0 + n < s1 ? idx[s0 + n] : -1;
   for (int t0 = s0; t0 < s1; t0 += 32) {
     // this lane's key row (A operand row n) and its validity
-    const int slot = t0 + n;
-    const int pos = slot < s1 ? idx[slot] : -1;
+    const int pos = pos_next;
     const bool valid = pos >= 0 && pos < a.seq_len;
     const uint32_t vmask = (uint32_t)__ballot(valid);  // bit j: key row j of the tile is valid
+    // the tile's value rows go to LDS: piece p = lane + 64 i is 16 bytes of row p / 16
+    int rp[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rp[i] = __shfl(pos, (lane + 64 * i) >> 4);
+    // all of the tile's gathers are issued before any of them is used (the
+    // compiler would otherwise place each next to its use and wait for it)
     i32x4 kf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       kf[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                              kr, valid ? (pos * kAD + 16 * ks + 8 * hf) * 2 : 0x80000000u, 0, 0));
-    // the tile's value rows into LDS: piece p = lane + 64 i is 16 bytes of row p / 16
     u32x4 vv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int p = lane + 64 * i, row = p >> 4, ch = p & 15;
-      const int rp = __shfl(pos, row);
       const bool rv = (vmask >> row) & 1u;
-      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, rv ? (rp * kADV + 8 * ch) * 2 : 0x80000000u, 0, 0);
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, rv ? (rp[i] * kADV + 8 * ch) * 2 : 0x80000000u, 0, 0);
     }
+    pos_next = t0 + 32 + n < s1 ? idx[t0 + 32 + n] : -1;
+    __builtin_amdgcn_sched_barrier(0);
     // scores S^T (32 keys x 32 heads per head block)
     f32x16 s[HB];
 #pragma unroll
@@ -227,37 +234,26 @@ __global__ __launch_bounds__(kWave) void sattn_kernel(SAttnArgs a) {
   }
 }
 
-// Merges the chunks of one row: with M the largest chunk maximum of a head,
-// out = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c (zeros for an empty row).
-constexpr int kCombineThreads = 256;
-__global__ __launch_bounds__(kCombineThreads) void sattn_combine_kernel(SAttnArgs a) {
-  __shared__ float sm[64], sinv[64];
-  const int r = blockIdx.x, tid = threadIdx.x;
+// Merges the chunks of one (row, head): with M the largest chunk maximum,
+// out = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c (zeros when the row
+// selected nothing).  One thread per value column; the chunk loop is unrolled
+// so that the chunks' loads are in flight together.
+__global__ __launch_bounds__(kADV) void sattn_combine_kernel(SAttnArgs a) {
+  const int r = blockIdx.y, h = blockIdx.x, col = threadIdx.x;
   const size_t p0 = (size_t)r * a.nch;
-  if (tid < a.Hq) {
-    float M = -INFINITY;
-    for (int c = 0; c < a.nch; ++c) M = fmaxf(M, a.part_ml[(p0 + c) * 2 * a.Hq + tid]);
-    float L = 0.f;
-    if (M != -INFINITY)
-      for (int c = 0; c < a.nch; ++c) {
-        const float* ml = a.part_ml + (p0 + c) * 2 * a.Hq;
-        L += __expf(ml[tid] - M) * ml[a.Hq + tid];
-      }
-    sm[tid] = M;
-    sinv[tid] = L > 0.f ? 1.f / L : 0.f;
+  float M = -INFINITY;
+  for (int c = 0; c < a.nch; ++c) M = fmaxf(M, a.part_ml[(p0 + c) * 2 * a.Hq + h]);
+  float acc = 0.f, L = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 8
+    for (int c = 0; c < a.nch; ++c) {
+      const float* ml = a.part_ml + (p0 + c) * 2 * a.Hq;
+      const float wgt = __expf(ml[h] - M);
+      L += wgt * ml[a.Hq + h];
+      acc += wgt * a.part_o[((p0 + c) * a.Hq + h) * kADV + col];
+    }
   }
-  __syncthreads();
-  for (int e = tid; e < a.Hq * kADV; e += kCombineThreads) {
-    const int h = e / kADV;
-    const float M = sm[h];
-    float acc = 0.f;
-    if (M != -INFINITY)
-      for (int c = 0; c < a.nch; ++c) {
-        const float mc = a.part_ml[(p0 + c) * 2 * a.Hq + h];
-        acc += __expf(mc - M) * a.part_o[((p0 + c) * a.Hq) * kADV + e];
-      }
-    a.out[(size_t)r * a.Hq * kADV + e] = acc * sinv[h];
-  }
+  a.out[((size_t)r * a.Hq + h) * kADV + col] = L > 0.f ? acc / L : 0.f;
 }
 
 }  // namespace
@@ -273,7 +269,7 @@ hipError_t launch_sparse_attention(const SAttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(sattn_kernel<2>, grid, dim3(kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nch == 1) return e;
-  hipLaunchKernelGGL(sattn_combine_kernel, dim3(a.R), dim3(kCombineThreads), 0, st, a);
+  hipLaunchKernelGGL(sattn_combine_kernel, dim3(a.Hq, a.R), dim3(kADV), 0, st, a);
   return hipGetLastError();
 }
 
