@@ -450,6 +450,19 @@ def main():
         del d, ws, out
         torch.cuda.empty_cache()
 
+        # several sequences of different lengths in one call (Refine g=8): the
+        # 16K workload's distributions, cut into sequences of 8K, 4K, 2K, 1K, 512, 256, 256
+        inp_v = synth.make("dsa_prefill_16k")
+        dv_ = upload(inp_v, torch)
+        lens = [8192, 4096, 2048, 1024, 512, 256, 256]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        out_v = torch.empty((16384, topk), dtype=torch.int32, device="cuda")
+        s_v = time_steps(lambda: pv.indexer_varlen(dv_["q"], dv_["w"], dv_["k"], cu, g=8, topk=topk, C=C,
+                                                   mode="refine", out=out_v), 5, 2, torch)
+        extras["varlen_refine_g8"] = {"lengths": lens, "ms_per_call": s_v * 1e3,
+                                      "queries_per_s": 16384 / s_v}
+        del dv_, out_v
+        torch.cuda.empty_cache()
         extras["decode"] = measure_decode(torch, pv, synth, 200, 100)
         extras["sparse_attention"] = measure_attention(torch, pv, synth)
         extras["pages_claims_context"] = ("up to 4x indexer speedup, about 3x for Refine, "

@@ -156,6 +156,28 @@ int pivot_indexer_decode_window(const void* q, const float* q_scale, const float
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Several prefill sequences of different lengths in one call.  Sequence i
+ * holds rows cu_seqlens[i] .. cu_seqlens[i+1]-1 of q, w, k (and the scales):
+ * its queries see only its own keys (position t of the sequence sees its keys
+ * 0..t), and its groups start at its first row.  Every sequence's rows are
+ * exactly those pivot_indexer_window would give for that sequence alone.
+ *
+ *   cu_seqlens  [nseq + 1] int64, HOST memory, cu_seqlens[0] = 0, non-decreasing
+ *               (a zero-length sequence is allowed)
+ *   out         [cu_seqlens[nseq]][topk + window] int32
+ *   window, window_mode as for pivot_indexer_window (window = 0: none)
+ * The workspace must hold pivot_varlen_workspace_size bytes (the size for the
+ * longest sequence).  All sequences are validated before anything is enqueued;
+ * they then run one after another on `stream`.
+ * ------------------------------------------------------------------------- */
+size_t pivot_varlen_workspace_size(const int64_t* cu_seqlens, int nseq, int H, int D, int g, int topk,
+                                   int C, int mode, int dtype);
+int pivot_indexer_varlen(const void* q, const float* q_scale, const float* w, const void* k,
+                         const float* k_scale, const int64_t* cu_seqlens, int nseq, int H, int D, int g,
+                         int topk, int C, int mode, int dtype, int window, int window_mode, int32_t* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sparse main attention over the selected positions (tutorial "Sparse
  * Attention의 Indexer", text after Figure 1): the main query of a row scores
  * the main keys at the positions the indexer selected and combines the values

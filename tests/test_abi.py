@@ -161,3 +161,26 @@ def test_sparse_attention_validation(lib):
     assert f() == ERR_WORKSPACE                 # 64 rows: chunks merged through the workspace
     assert lib.pivot_sparse_attention_workspace_size(64, 64, 128, 2048) > 0
     assert lib.pivot_sparse_attention_workspace_size(4096, 64, 128, 2048) == 0  # one chunk per row
+
+
+def test_varlen_validation(lib):
+    import ctypes
+    import numpy as np
+
+    def f(cu, **kw):
+        a = dict(q=FAKE, w=FAKE, k=FAKE, out=FAKE, wsb=1 << 40, mode=pv.REFINE)
+        a.update(kw)
+        arr = None if cu is None else np.ascontiguousarray(cu, np.int64)
+        return lib.pivot_indexer_varlen(a["q"], None, a["w"], a["k"], None,
+                                        None if arr is None else arr.ctypes.data, 0 if cu is None else len(cu) - 1,
+                                        4, 32, 4, 64, 256, a["mode"], 0, 0, 0, a["out"], FAKE, a["wsb"], None)
+    assert f(None) == ERR_NULL
+    assert f([0]) == ERR_SHAPE                   # no sequence
+    assert f([1, 5]) == ERR_PARAM                # must start at 0
+    assert f([0, 9, 5]) == ERR_PARAM             # decreasing
+    assert f([0, 9, 20], out=None) == ERR_NULL
+    assert f([0, 9, 20], mode=9) == ERR_PARAM
+    assert f([0, 2048, 4096], wsb=1000) == ERR_WORKSPACE
+    cu = np.array([0, 100, 100, 3000], np.int64)
+    big = lib.pivot_varlen_workspace_size(cu.ctypes.data, 3, 4, 32, 4, 64, 256, pv.REFINE, 0)
+    assert big == lib.pivot_workspace_size(2900, 4, 32, 4, 64, 256, pv.REFINE, 0)

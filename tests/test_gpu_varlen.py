@@ -1,0 +1,64 @@
+"""GPU parity of several prefill sequences in one call (variable lengths, one
+after another in the inputs): every sequence's rows must equal the oracle's for
+that sequence alone (integer-valued inputs: bit for bit), in every mode, with
+and without a sliding window, including empty and one-token sequences."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_token_selection_pivot_amd as pv
+from parity import to_device
+
+pytestmark = pytest.mark.gpu
+
+LENS = [37, 0, 1, 700, 2048, 5, 300]
+
+
+@pytest.fixture(scope="module")
+def batch():
+    inp = synth.small_integer(sum(LENS), 4, 32, seed=77, qmax=2, kmax=2, wmax=3)
+    cu = np.concatenate([[0], np.cumsum(LENS)]).astype(np.int64)
+    return inp, cu
+
+
+def _seq_view(inp, a, b):
+    return oracle.View("bf16", inp.q[a:b], None, inp.w[a:b], inp.k[a:b], None)
+
+
+@pytest.mark.parametrize("W,wmode", [(0, "shared"), (16, "shared"), (16, "excluded")])
+@pytest.mark.parametrize("mode", ["dense", "reuse", "refine"])
+def test_varlen_bit_exact(batch, mode, W, wmode):
+    print(f"case: varlen prefill lengths {LENS} g=4 k=24 C=60 {mode} window {W} {wmode}", flush=True)
+    inp, cu = batch
+    d = to_device(inp)
+    got = pv.indexer_varlen(d["q"], d["w"], d["k"], cu, g=4, topk=24, C=60, mode=mode, window=W,
+                            window_mode=wmode).cpu().numpy()
+    assert got.shape == (cu[-1], 24 + W)
+    for i, L in enumerate(LENS):
+        if L == 0:
+            continue
+        a, b = int(cu[i]), int(cu[i + 1])
+        v = _seq_view(inp, a, b)
+        excl = W if wmode == "excluded" else 0
+        if mode == "dense":
+            sel = oracle.dense_rows(v, np.arange(L), 24, excl=excl)
+        else:
+            sel, _ = oracle.prefill_groups(v, L, 4, 24, 60, mode, np.arange((L + 3) // 4), excl=excl)
+        ref = oracle.window_union(sel, np.arange(L), W) if W else sel
+        assert np.array_equal(got[a:b], ref), (mode, i)
+
+
+def test_varlen_equals_separate_calls(batch):
+    print("case: varlen == one call per sequence (Refine g=4)", flush=True)
+    inp, cu = batch
+    d = to_device(inp)
+    got = pv.indexer_varlen(d["q"], d["w"], d["k"], cu, g=4, topk=24, C=60, mode="refine")
+    for i, L in enumerate(LENS):
+        if L == 0:
+            continue
+        a, b = int(cu[i]), int(cu[i + 1])
+        one = pv.indexer(d["q"][a:b].contiguous(), d["w"][a:b].contiguous(), d["k"][a:b].contiguous(),
+                         g=4, topk=24, C=60, mode="refine")
+        assert torch.equal(got[a:b], one), i

@@ -83,6 +83,10 @@ def load():
     L.pivot_sparse_attention.restype = i
     L.pivot_sparse_attention.argtypes = [vp, vp, vp, ip] + [i] * 6 + [C.c_longlong, i, C.c_float,
                                                                       fp, vp, sz, vp]
+    L.pivot_varlen_workspace_size.restype = sz
+    L.pivot_varlen_workspace_size.argtypes = [vp] + [i] * 8
+    L.pivot_indexer_varlen.restype = i
+    L.pivot_indexer_varlen.argtypes = [vp, fp, fp, vp, fp, vp] + [i] * 10 + [ip, vp, sz, vp]
     L.pivot_decode_candidates.restype = i
     L.pivot_decode_candidates.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, vp, sz, vp]
     L.pivot_profile_enable.restype = i
@@ -191,6 +195,33 @@ def indexer(q, w, k, *, g: int, topk: int, C: int = 0, mode="refine", q_scale=No
     else:
         _check(L.pivot_indexer(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), Lq, H, D,
                                g, topk, C, m, dt, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def indexer_varlen(q, w, k, cu_seqlens, *, g: int, topk: int, C: int = 0, mode="refine",
+                   q_scale=None, k_scale=None, window: int = 0, window_mode="shared", out=None,
+                   workspace=None, stream=None) -> torch.Tensor:
+    """Several prefill sequences in one call (pivot_indexer_varlen): q [T,H,D],
+    w [T,H], k [T,D] hold the sequences back to back; cu_seqlens (host ints,
+    nseq + 1 offsets starting at 0) delimits them.  Returns int32
+    [T, topk + window]; each sequence's rows are those of indexer() on it alone."""
+    import numpy as np
+    L = load()
+    q, w, k = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k, "k")
+    q_scale, k_scale = _dev(q_scale, "q_scale", torch.float32), _dev(k_scale, "k_scale", torch.float32)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    nseq = cu.shape[0] - 1
+    T, H, D = q.shape
+    dt = _dtype_of(q)
+    m = _mode(mode)
+    if out is None:
+        out = torch.empty((T, topk + window), dtype=torch.int32, device=q.device)
+    ws = _workspace(L.pivot_varlen_workspace_size(cu.ctypes.data, nseq, H, D, g, topk, C, m, dt),
+                    q.device, workspace)
+    _check(L.pivot_indexer_varlen(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale),
+                                  cu.ctypes.data, nseq, H, D, g, topk, C, m, dt, window,
+                                  _window_mode(window_mode), _ptr(out), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
     return out
 
 

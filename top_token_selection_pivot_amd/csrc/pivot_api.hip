@@ -399,6 +399,67 @@ int pivot_indexer(const void* q, const float* q_scale, const float* w, const voi
                      workspace, workspace_bytes, stream);
 }
 
+size_t pivot_varlen_workspace_size(const int64_t* cu_seqlens, int nseq, int H, int D, int g, int topk,
+                                   int C, int mode, int dtype) {
+  if (!cu_seqlens || nseq < 1) return 0;
+  int Lmax = 0;
+  for (int i = 0; i < nseq; ++i) {
+    const int64_t n = cu_seqlens[i + 1] - cu_seqlens[i];
+    if (n < 0 || n > INT32_MAX) return 0;
+    Lmax = std::max<int>(Lmax, (int)n);
+  }
+  return Lmax > 0 ? pivot_workspace_size(Lmax, H, D, g, topk, C, mode, dtype) : 256;
+}
+
+int pivot_indexer_varlen(const void* q, const float* q_scale, const float* w, const void* k,
+                         const float* k_scale, const int64_t* cu_seqlens, int nseq, int H, int D, int g,
+                         int topk, int C, int mode, int dtype, int window, int window_mode, int32_t* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return fail(PIVOT_ERR_NULL, "cu_seqlens must be non-NULL (host memory)");
+  if (nseq < 1) return fail(PIVOT_ERR_SHAPE, "nseq=%d must be >= 1", nseq);
+  if (cu_seqlens[0] != 0) return fail(PIVOT_ERR_PARAM, "cu_seqlens[0] must be 0");
+  for (int i = 0; i < nseq; ++i) {
+    const int64_t n = cu_seqlens[i + 1] - cu_seqlens[i];
+    if (n < 0 || n > INT32_MAX)
+      return fail(PIVOT_ERR_PARAM, "sequence %d has length %lld", i, (long long)n);
+  }
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  // every sequence is checked before anything is enqueued
+  int st = validate_common(q, q_scale, w, k, k_scale, H, D, g, topk, C, mode, dtype);
+  if (st) return st;
+  st = validate_window(window, window_mode, topk);
+  if (st) return st;
+  const size_t esz = esize(dtype);
+  for (int i = 0; i < nseq; ++i) {
+    const int64_t t0 = cu_seqlens[i];
+    const int L = (int)(cu_seqlens[i + 1] - t0);
+    if (L == 0) continue;
+    const size_t qoff = (size_t)t0 * H * D * esz, koff = (size_t)t0 * D * esz;
+    if (!aligned((const uint8_t*)q + qoff, 16) || !aligned((const uint8_t*)k + koff, 16))
+      return fail(PIVOT_ERR_ALIGN, "sequence %d: q and k rows must stay 16-byte aligned", i);
+    if ((long long)L * D * esz >= (1ll << 31))
+      return fail(PIVOT_ERR_SHAPE, "sequence %d: the key array must stay below 2 GiB", i);
+    const bool dense = mode == PIVOT_MODE_DENSE;
+    const PrefillPlan p = plan_prefill(L, H, D, dense ? 1 : g, topk, C, mode, dtype);
+    if (chunk_rows_for(p, workspace_bytes, dense) <= 0)
+      return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu for sequence %d",
+                  workspace_bytes, prefill_bytes(p, std::min(p.G, 8), dense), i);
+  }
+  // the sequences run one after another on the stream, each through the
+  // whole prefill path with its own causal prefix and groups
+  for (int i = 0; i < nseq; ++i) {
+    const int64_t t0 = cu_seqlens[i];
+    const int L = (int)(cu_seqlens[i + 1] - t0);
+    if (L == 0) continue;
+    st = run_prefill((const uint8_t*)q + (size_t)t0 * H * D * esz, q_scale ? q_scale + t0 : nullptr,
+                     w + (size_t)t0 * H, (const uint8_t*)k + (size_t)t0 * D * esz, k_scale ? k_scale + t0 : nullptr,
+                     L, H, D, g, topk, C, mode, dtype, out + (size_t)t0 * (topk + window), nullptr, workspace,
+                     workspace_bytes, stream, window, window_mode);
+    if (st) return st;
+  }
+  return PIVOT_OK;
+}
+
 int pivot_candidates(const void* q, const float* q_scale, const float* w, const void* k,
                      const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
                      int dtype, int32_t* cand, void* workspace, size_t workspace_bytes,
