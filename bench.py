@@ -121,6 +121,28 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
     key_bytes = float(dec.cache_len.astype(np.int64).sum()) * (D + 4)
     scan_ms_d = dprof["decode_scan"][0] / nd_prof
     dense_dsec = time_steps(lambda: dstep("dense"), max(1, nd_steps // 2), 5, torch)
+    # the same step over a paged cache: 64-key pages of a shuffled pool
+    log("laying the decode cache out in 64-key pages")
+    pc = synth.paged_cache(dec, 64)
+    kp = torch.from_numpy(pc.k_pages).cuda()
+    ksp = torch.from_numpy(pc.k_scale_pages).cuda()
+    btd = torch.from_numpy(pc.block_table).cuda()
+
+    def pstep():
+        pv.indexer_decode_paged(dd["q"], dd["w"], kp, btd, dd["cache_len"], topk=topk, C=C,
+                                mode="refine", q_scale=dd["q_scale"], k_scale=ksp, out=dout,
+                                workspace=dws)
+
+    paged_sec = time_steps(pstep, nd_steps, 10, torch)
+    pv.profile_enable(True)
+    pv.profile_read()
+    for _ in range(nd_prof):
+        pstep()
+    torch.cuda.synchronize()
+    pprof = pv.profile_read()
+    pv.profile_enable(False)
+    pscan_ms = pprof["decode_scan"][0] / nd_prof
+    del kp, ksp, btd, pc
     # a deeper multi-token-prediction group: four queries per sequence, same
     # cache lengths and distributions
     del dd, dws, dout
@@ -141,6 +163,10 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
         "us_per_step": dsec * 1e6,
         "dense_us_per_step": dense_dsec * 1e6,
         "refine_g4_us_per_step": g4_sec * 1e6,
+        "paged64_us_per_step": paged_sec * 1e6,
+        "paged64_decode_scan_us": pscan_ms * 1e3,
+        "paged64_decode_scan_hbm_GBs": key_bytes / (pscan_ms / 1e3) / 1e9,
+        "paged64_refine_us": pprof["refine_score"][0] / nd_prof * 1e3,
         "key_stream_bytes": key_bytes,
         "decode_scan_us": scan_ms_d * 1e3,
         "decode_scan_hbm_GBs": key_bytes / (scan_ms_d / 1e3) / 1e9,
@@ -148,7 +174,8 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
         "kernels_us": {k: v[0] / nd_prof * 1e3 for k, v in dprof.items() if v[1]},
     }
     log(f"decode {dsec*1e6:.1f} us/step; scan {key_bytes/(scan_ms_d/1e3)/1e9:.0f} GB/s; "
-        f"g=4 {g4_sec*1e6:.1f} us/step")
+        f"g=4 {g4_sec*1e6:.1f} us/step; paged (64) {paged_sec*1e6:.1f} us/step, "
+        f"scan {pscan_ms*1e3:.1f} us")
     torch.cuda.empty_cache()
     return res
 

@@ -156,6 +156,35 @@ int pivot_indexer_decode_window(const void* q, const float* q_scale, const float
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * One decode step (as pivot_indexer_decode_window) over a paged indexer-key
+ * cache, as a server keeps it: the keys of every sequence live in pages of a
+ * shared pool, and a block table lists each sequence's pages in order.  The
+ * result is the one pivot_indexer_decode_window gives for the contiguous cache
+ * whose position p of sequence b holds the pool row
+ *     block_table[b][p / page_size] * page_size + p % page_size.
+ *
+ *   k_pages        [num_pages][page_size][D] codes (16-byte aligned)
+ *   k_scale_pages  [num_pages][page_size] float (fp8 only, else NULL)
+ *   block_table    [B][max_pages] int32, DEVICE memory: the first
+ *                  ceil(cache_len[b] / page_size) entries of row b are page
+ *                  ids; an id outside [0, num_pages) reads as a page of zero
+ *                  keys (scores 0), never out of bounds
+ *   page_size      a power of two, 64 .. 2^20 (every 64-key tile pair of the
+ *                  scan lies in one page)
+ *   cache_len      [B] int32, DEVICE memory; g <= cache_len[b] <=
+ *                  max_pages * page_size, else the sequence's rows are -1
+ * The pool must stay below 4 GiB of key codes.  The workspace is
+ * pivot_decode_workspace_size(B, max_pages * page_size, ...) bytes.  Other
+ * arguments as for pivot_indexer_decode_window (window = 0: none).
+ * ------------------------------------------------------------------------- */
+int pivot_indexer_decode_paged(const void* q, const float* q_scale, const float* w, const void* k_pages,
+                               const float* k_scale_pages, int num_pages, int page_size,
+                               const int32_t* block_table, int max_pages, const int32_t* cache_len, int B,
+                               int H, int D, int g, int topk, int C, int mode, int dtype, int window,
+                               int window_mode, int32_t* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------
  * Several prefill sequences of different lengths in one call.  Sequence i
  * holds rows cu_seqlens[i] .. cu_seqlens[i+1]-1 of q, w, k (and the scales):
  * its queries see only its own keys (position t of the sequence sees its keys

@@ -6,7 +6,7 @@ lives in pivot_oracle.c (plain single-threaded C, double accumulation); this
 file only marshals numpy arrays.
 
 Pinned functions (see tests/test_oracle_*.py): codecs, score, top-m, dense,
-proxy, Reuse, Refine, decode grouping, sliding-window union and exclusion.  Parity on realistic float inputs is
+proxy, Reuse, Refine, decode grouping, sliding-window union and exclusion, the paged-cache view.  Parity on realistic float inputs is
 pinned only through invariants and the closed-form/worked examples.
 """
 from __future__ import annotations
@@ -265,6 +265,29 @@ def decode_seq(dec, b: int, topk_: int, C_: int, mode):
     shared scan covers the whole cache [0, n_b)."""
     n = int(dec.cache_len[b])
     return group(decode_view(dec, b), 0, n - dec.g, dec.g, topk_, C_, mode)
+
+
+def paged_keys(k_pages, k_scale_pages, block_table, cache_len, Lmax: int):
+    """The contiguous key cache [B, Lmax, D] (scales [B, Lmax], or None) that a
+    paged cache stands for.  Position p < cache_len[b] of sequence b is row
+    p % page_size of page block_table[b, p // page_size]; a page id outside
+    [0, num_pages) stands for zero keys with zero scales; positions past
+    cache_len[b] are zero.  Paging is a storage layout, not part of the
+    method: a decode step over a paged cache is defined as the step over this
+    contiguous cache (decode grouping as in decode_seq)."""
+    k_pages = np.asarray(k_pages)
+    num_pages, page_size, D = k_pages.shape
+    B = block_table.shape[0]
+    k = np.zeros((B, Lmax, D), k_pages.dtype)
+    ks = None if k_scale_pages is None else np.zeros((B, Lmax), np.float32)
+    for b in range(B):
+        for p in range(int(cache_len[b])):
+            pg = int(block_table[b, p // page_size])
+            if 0 <= pg < num_pages:
+                k[b, p] = k_pages[pg, p % page_size]
+                if ks is not None:
+                    ks[b, p] = k_scale_pages[pg, p % page_size]
+    return k, ks
 
 
 def sparse_attention(q, k, v, idx, rows_per_seq=None, seq_len=None, scale=None):

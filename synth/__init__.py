@@ -31,6 +31,8 @@ __all__ = [
     "small_integer",
     "dsa_prefill",
     "decode_mtp",
+    "PagedCache",
+    "paged_cache",
     "CONFIGS",
 ]
 
@@ -218,6 +220,57 @@ def decode_mtp(B=32, Lmin=32768, Lmax=131072, H=64, D=128, g=2, seed=1005,
         return DecodeInputs("bf16", B, Lmax, H, D, g, encode_bf16(qf), None, w, k, None, cache_len)
     qc, qs = encode_fp8_per_row(qf, 2)
     return DecodeInputs("fp8", B, Lmax, H, D, g, qc, qs, w, k, k_scale, cache_len)
+
+
+@dataclass
+class PagedCache:
+    """A decode step's key cache laid out in pages of a shared pool.
+
+    k_pages: [num_pages, page_size, D] codes; k_scale_pages: [num_pages,
+    page_size] (fp8 only); block_table: [B, max_pages] int32, row b listing the
+    pages that hold positions 0.., page_size at a time (-1 past them)."""
+
+    page_size: int
+    k_pages: np.ndarray
+    k_scale_pages: Optional[np.ndarray]
+    block_table: np.ndarray
+
+
+def paged_cache(dec: DecodeInputs, page_size: int, seed: int = 2001,
+                spare_pages: int = 3) -> PagedCache:
+    """Scatter dec's key cache into pages of a pool in a random order, as a
+    server's allocator leaves it.  Every byte that is not a cached key (the
+    spare pages, the tail of each sequence's last page) holds random codes and
+    random scales, so that a wrong page or a read past a sequence's end shows."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    npg = [(int(n) + page_size - 1) // page_size for n in dec.cache_len]
+    max_pages = (dec.Lmax + page_size - 1) // page_size
+    num_pages = sum(npg) + spare_pages
+    perm = rng.permutation(num_pages).astype(np.int32)
+    esz = dec.k.dtype
+    kp = rng.integers(0, np.iinfo(esz).max, size=(num_pages, page_size, dec.D), dtype=esz,
+                      endpoint=True)
+    if dec.dtype == "bf16":  # random finite bf16 codes of moderate size
+        kp &= np.uint16(0x807F)
+        kp |= np.uint16(0x3E00)
+    else:  # random finite E4M3FN codes (0x7F / 0xFF are NaN)
+        kp[(kp & 0x7F) == 0x7F] &= np.uint8(0xF0)
+    ksp = None
+    if dec.k_scale is not None:
+        ksp = rng.uniform(0.5, 2.0, size=(num_pages, page_size)).astype(np.float32)
+    bt = np.full((dec.B, max_pages), -1, np.int32)
+    used = 0
+    for b in range(dec.B):
+        n = int(dec.cache_len[b])
+        for i in range(npg[b]):
+            pg = int(perm[used])
+            used += 1
+            bt[b, i] = pg
+            lo, hi = i * page_size, min(n, (i + 1) * page_size)
+            kp[pg, : hi - lo] = dec.k[b, lo:hi]
+            if ksp is not None:
+                ksp[pg, : hi - lo] = dec.k_scale[b, lo:hi]
+    return PagedCache(page_size, kp, ksp, bt)
 
 
 # The five workloads: name -> (kind, parameters).

@@ -184,3 +184,29 @@ def test_varlen_validation(lib):
     cu = np.array([0, 100, 100, 3000], np.int64)
     big = lib.pivot_varlen_workspace_size(cu.ctypes.data, 3, 4, 32, 4, 64, 256, pv.REFINE, 0)
     assert big == lib.pivot_workspace_size(2900, 4, 32, 4, 64, 256, pv.REFINE, 0)
+
+
+def test_paged_decode_validation(lib):
+    # the paged decode entry checks the pool and the block table before
+    # anything runs; with valid pages it fails only on the workspace
+    def f(**kw):
+        a = dict(num_pages=2100, page_size=64, bt=FAKE, max_pages=2048, D=128, dt=1, wsb=100,
+                 out=FAKE, ks=FAKE)
+        a.update(kw)
+        return lib.pivot_indexer_decode_paged(FAKE, FAKE, FAKE, FAKE, a["ks"], a["num_pages"],
+                                              a["page_size"], a["bt"], a["max_pages"], FAKE, 32, 64,
+                                              a["D"], 2, 2048, 4096, pv.REFINE, a["dt"], 0, 0,
+                                              a["out"], FAKE, a["wsb"], None)
+    assert f() == ERR_WORKSPACE
+    assert f(page_size=1024, max_pages=128) == ERR_WORKSPACE
+    assert f(bt=None) == ERR_NULL
+    assert f(out=None) == ERR_NULL
+    assert f(ks=None) == ERR_NULL  # fp8 needs the pool's scales
+    assert f(bt=FAKE + 2) == ERR_ALIGN
+    for ps in (0, 32, 96, 1 << 21):
+        assert f(page_size=ps) == ERR_PARAM, ps
+    assert f(num_pages=0) == ERR_SHAPE
+    assert f(max_pages=0) == ERR_SHAPE
+    # the pool must stay below 4 GiB of key codes: 2^26 keys of 64 bytes is 4 GiB
+    assert f(num_pages=1 << 20, page_size=64, D=64) == ERR_SHAPE
+    assert f(num_pages=(1 << 20) - 1, page_size=64, D=64) == ERR_WORKSPACE

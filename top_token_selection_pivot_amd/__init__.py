@@ -23,7 +23,8 @@ import torch
 
 __all__ = [
     "DENSE", "REUSE", "REFINE", "PivotError", "library_path", "load",
-    "indexer", "indexer_decode", "proxy_mean", "candidates", "decode_candidates",
+    "indexer", "indexer_decode", "indexer_decode_paged", "indexer_varlen",
+    "sparse_attention", "proxy_mean", "candidates", "decode_candidates",
     "workspace_size",
     "decode_workspace_size", "selftest_mfma_layout",
 ]
@@ -88,6 +89,8 @@ def load():
     L.pivot_indexer_varlen.restype = i
     L.pivot_indexer_varlen.argtypes = [vp, fp, fp, vp, fp, vp] + [i] * 10 + [ip, vp, sz, vp]
     L.pivot_decode_candidates.restype = i
+    L.pivot_indexer_decode_paged.argtypes = [vp, fp, fp, vp, fp, i, i, ip, i, ip] + [i] * 10 + [ip, vp, sz, vp]
+    L.pivot_indexer_decode_paged.restype = i
     L.pivot_decode_candidates.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, vp, sz, vp]
     L.pivot_profile_enable.restype = i
     L.pivot_profile_enable.argtypes = [i]
@@ -285,6 +288,38 @@ def indexer_decode(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="ref
         _check(L.pivot_indexer_decode(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache),
                                       _ptr(k_scale), _ptr(cache_len), B, Lmax, H, D, g, topk, C, m,
                                       dt, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def indexer_decode_paged(q, w, k_pages, block_table, cache_len, *, topk: int, C: int = 0,
+                         mode="refine", q_scale=None, k_scale=None, window: int = 0,
+                         window_mode="shared", out=None, workspace=None,
+                         stream=None) -> torch.Tensor:
+    """One MTP decode step over a paged key cache (pivot_indexer_decode_paged).
+
+    k_pages [num_pages, page_size, D] codes (fp8: k_scale [num_pages,
+    page_size]); block_table [B, max_pages] int32 page ids (device); position
+    p of sequence b is row p % page_size of page block_table[b, p //
+    page_size].  Other arguments as for indexer_decode.  Returns int32
+    [B, g, topk + window]."""
+    L = load()
+    q, w, k_pages = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k_pages, "k_pages")
+    block_table = _dev(block_table, "block_table", torch.int32)
+    cache_len = _dev(cache_len, "cache_len", torch.int32)
+    B, g, H, D = q.shape
+    num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
+    max_pages = block_table.shape[1]
+    dt = _dtype_of(q)
+    m = _mode(mode)
+    if out is None:
+        out = torch.empty((B, g, topk + window), dtype=torch.int32, device=q.device)
+    ws = _workspace(L.pivot_decode_workspace_size(B, max_pages * page_size, H, D, g, topk, C, m, dt),
+                    q.device, workspace)
+    _check(L.pivot_indexer_decode_paged(
+        _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_pages), _ptr(k_scale), num_pages, page_size,
+        _ptr(block_table), max_pages, _ptr(cache_len), B, H, D, g, topk, C, m, dt, window,
+        _window_mode(window_mode), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
     return out
 
 

@@ -490,15 +490,46 @@ size_t pivot_decode_workspace_size(int B, int Lmax, int H, int D, int g, int top
   return plan_decode(B, Lmax, H, D, g, topk, C, mode, dtype).total + kAlign;
 }
 
+// A paged key cache: a pool of num_pages pages of page_size keys (k_cache and
+// k_scale point at the pool) and a block table of max_pages page ids per sequence.
+struct PagedKeys {
+  const int32_t* bt;
+  int max_pages, page_size, num_pages;
+};
+
+static int validate_pages(const PagedKeys& pk, int D, int dtype) {
+  if (!pk.bt) return fail(PIVOT_ERR_NULL, "block_table must be non-NULL");
+  if (!aligned(pk.bt, 4)) return fail(PIVOT_ERR_ALIGN, "block_table must be 4-byte aligned");
+  if (pk.page_size < 64 || pk.page_size > (1 << 20) || (pk.page_size & (pk.page_size - 1)))
+    return fail(PIVOT_ERR_PARAM, "page_size=%d must be a power of two in 64..2^20", pk.page_size);
+  if (pk.num_pages < 1 || pk.max_pages < 1)
+    return fail(PIVOT_ERR_SHAPE, "num_pages=%d and max_pages=%d must be >= 1", pk.num_pages, pk.max_pages);
+  if ((long long)pk.max_pages * pk.page_size > INT32_MAX / 2)
+    return fail(PIVOT_ERR_SHAPE, "max_pages * page_size too large");
+  if ((long long)pk.num_pages * pk.page_size * D * esize(dtype) >= (1ll << 32))
+    return fail(PIVOT_ERR_SHAPE, "the key pool (num_pages * page_size * D codes) must stay below 4 GiB");
+  return PIVOT_OK;
+}
+
+static void set_pages(DecScanArgs& da, const PagedKeys* pk) {
+  if (!pk) return;
+  da.bt = pk->bt;
+  da.bt_stride = pk->max_pages;
+  da.page_shift = __builtin_ctz((unsigned)pk->page_size);
+  da.num_pages = pk->num_pages;
+}
+
 static int run_decode(const void* q, const float* q_scale, const float* w,
                       const void* k_cache, const float* k_scale, const int32_t* cache_len,
                       int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
                       int dtype, int32_t* out, int32_t* cand_user, void* workspace,
-                      size_t workspace_bytes, void* stream, int window = 0, int wmode = 0) {
+                      size_t workspace_bytes, void* stream, int window = 0, int wmode = 0,
+                      const PagedKeys* pk = nullptr) {
   int st = validate_common(q, q_scale, w, k_cache, k_scale, H, D, g, topk, C, mode, dtype);
   if (st) return st;
   st = validate_window(window, wmode, topk);
   if (st) return st;
+  if (pk && (st = validate_pages(*pk, D, dtype))) return st;
   const int excl = wmode == PIVOT_WINDOW_EXCLUDED ? window : 0;
   const long long ldo = (long long)topk + window;
   if (B < 1 || Lmax < 1) return fail(PIVOT_ERR_SHAPE, "B=%d and Lmax=%d must be >= 1", B, Lmax);
@@ -530,6 +561,7 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
     PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_fill_u32(hist, (size_t)p.rows * kSelectBins1, 0u, s),
                    "decode histogram clear");
     DecScanArgs da{qb, q_scale, w, kb, k_scale, Lmax, H, cache_len, g, g, S, p.ldS, hist, B, excl};
+    set_pages(da, pk);
     PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");
     sel.m = topk;
     sel.kind = kLenDecodeDense;
@@ -547,6 +579,7 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   ProxyArgs pa{qb, q_scale, w, B * g, H, D, g, qbar, qbs, wbar, hist, (size_t)p.rows * kSelectBins1};
   PIVOT_LAUNCH_K(PIVOT_K_PROXY, s, launch_proxy_mean(pa, dtype, s), "decode proxy mean");
   DecScanArgs da{qbar, qbs, wbar, kb, k_scale, Lmax, H, cache_len, g, 1, S, p.ldS, hist, B, excl};
+  set_pages(da, pk);
   PIVOT_LAUNCH_K(PIVOT_K_DECODE_SCAN, s, launch_decode_scan(da, dtype, D, s), "decode scan");
   sel.m = p.m;
   sel.kind = kLenCache;
@@ -563,6 +596,12 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   float* R = (float*)(ws + p.off_R);
   RefineArgs ra{qb, q_scale, w, kb, k_scale, H, 1, 0, g, Lmax, cache_len, 0, B, cand, p.m, p.m,
                 kRefineSlotChunk, R, p.ldR, 0, excl};
+  if (pk) {
+    ra.bt = pk->bt;
+    ra.bt_stride = pk->max_pages;
+    ra.page_shift = __builtin_ctz((unsigned)pk->page_size);
+    ra.pool_rows = pk->num_pages * pk->page_size;
+  }
   PIVOT_LAUNCH_K(PIVOT_K_REFINE, s, launch_refine(ra, dtype, D, s), "decode refine score");
   TopkArgs tr{};
   tr.S = R;
@@ -613,6 +652,20 @@ int pivot_indexer_decode_window(const void* q, const float* q_scale, const float
   if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
   return run_decode(q, q_scale, w, k_cache, k_scale, cache_len, B, Lmax, H, D, g, topk, C, mode,
                     dtype, out, nullptr, workspace, workspace_bytes, stream, window, window_mode);
+}
+
+int pivot_indexer_decode_paged(const void* q, const float* q_scale, const float* w, const void* k_pages,
+                               const float* k_scale_pages, int num_pages, int page_size,
+                               const int32_t* block_table, int max_pages, const int32_t* cache_len, int B,
+                               int H, int D, int g, int topk, int C, int mode, int dtype, int window,
+                               int window_mode, int32_t* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  const PagedKeys pk{block_table, max_pages, page_size, num_pages};
+  int st = validate_pages(pk, D, dtype);
+  if (st) return st;
+  return run_decode(q, q_scale, w, k_pages, k_scale_pages, cache_len, B, max_pages * page_size, H, D, g, topk, C,
+                    mode, dtype, out, nullptr, workspace, workspace_bytes, stream, window, window_mode, &pk);
 }
 
 int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,

@@ -60,6 +60,13 @@ struct RefineArgs {
   long long ldS;
   int row_base;
   int excl = 0;  // window excluded: every member's limit is its position - excl
+  // Decode with a paged key cache (bt non-NULL): position p of sequence j is
+  // row bt[j * bt_stride + (p >> page_shift)] * 2^page_shift + p % 2^page_shift
+  // of the pool k (k_scale), which holds pool_rows rows (below 4 GiB of keys);
+  // a page id outside [0, pool_rows >> page_shift) reads as zero keys.
+  const int32_t* bt = nullptr;
+  int bt_stride = 0, page_shift = 0;
+  int pool_rows = 0;
 };
 
 // Decode scan: for each sequence b, qr query rows (rows b*qr .. b*qr+qr-1 of
@@ -82,6 +89,11 @@ struct DecScanArgs {
   uint32_t* hist;
   int B;
   int excl = 0;  // window excluded: every row's limit moves down by excl
+  // paged key cache (bt non-NULL), addressed as in RefineArgs; pages hold a
+  // multiple of 64 keys so that every pair of 32-key tiles lies in one page
+  const int32_t* bt = nullptr;
+  int bt_stride = 0, page_shift = 0;
+  int num_pages = 0;
 };
 
 // Top-m of decode score rows with precomputed first-digit histograms: `parts`

@@ -244,8 +244,8 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
       row0 = j * a.g;
       nmem = a.g;
       ncand = min(a.m, max(0, nb - a.excl));
-      nkeys = nb;
-      keybase = (size_t)j * a.Lmax;
+      nkeys = a.bt ? a.pool_rows : nb;  // paged: the whole pool, slots translated below
+      keybase = a.bt ? 0 : (size_t)j * a.Lmax;
     }
     k0 = blockIdx.x * a.slot_chunk;
     if (k0 >= ncand) return;
@@ -276,9 +276,24 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
     }
   }
 
-  // key position of slot `slot` (Refine) -- 0 outside the workgroup's slots
+  // key row of slot `slot` (Refine) -- 0 outside the workgroup's slots.  With
+  // a paged cache the candidate positions become pool rows here; a page id
+  // outside the pool gives the row just past it, which reads as zeros.
   if constexpr (GATHER) {
-    for (int e = tid; e < k1 - k0; e += NT) cand_s[e] = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, e * 4, 0, 0);
+    for (int e = tid; e < k1 - k0; e += NT) {
+      int v = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, e * 4, 0, 0);
+      if constexpr (std::is_same_v<Args, RefineArgs>) {
+        if (a.bt) {
+          const int j = a.grp_begin + blockIdx.y;
+          v = max(v, 0);
+          const int pg = a.bt[(size_t)j * a.bt_stride + (v >> a.page_shift)];
+          v = (unsigned)pg < (unsigned)(a.pool_rows >> a.page_shift)
+                  ? (pg << a.page_shift) + (v & ((1 << a.page_shift) - 1))
+                  : a.pool_rows;
+        }
+      }
+      cand_s[e] = v;
+    }
     __syncthreads();
   }
   auto cand_pos = [&](int slot) -> int {
@@ -297,7 +312,7 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
         if constexpr (!GATHER)
           off = (base - k0) * KT::ROW + c * 16;
         else
-          off = cand_pos(base + c / RCH) * KT::ROW + (c % RCH) * 16;
+          off = (int)((uint32_t)cand_pos(base + c / RCH) * KT::ROW + (c % RCH) * 16);
         pre[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
       }
     }
@@ -393,6 +408,11 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
 // collected in LDS and written with one 16-byte-per-lane store, and the top 12
 // bits of their keys are histogrammed per row in LDS and added to the row's
 // histogram in memory whenever the run moves to the next sequence.
+//
+// With a paged cache (PAGED) a pair of tiles lies inside one page: each pair's
+// loads get a descriptor of their own, based at the pair's first key in its
+// page and ranged to the run's last key, from a page id read through the
+// scalar cache.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int QR>
 struct DecGeom {
@@ -417,7 +437,14 @@ struct DecGeom {
   static_assert(PAIR_BYTES % 1024 == 0 && fits(W, R) && (R - 1) * STAGE_OPS < 64);
 };
 
-template <int DT, int D, int HB, int QR>
+// A page id, read with a scalar load: the address is wave-uniform and the
+// block table is not written while the kernel runs.
+__device__ inline int page_id(const int32_t* bt, size_t i) {
+  typedef __attribute__((address_space(4))) const int32_t cint;
+  return __builtin_amdgcn_readfirstlane(((cint*)bt)[i]);
+}
+
+template <int DT, int D, int HB, int QR, bool PAGED>
 __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_kernel(DecScanArgs a) {
   using G = DecGeom<DT, D, QR>;
   using Frag = typename Fmt<DT>::frag;
@@ -467,7 +494,7 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
   for (int i = 0; i < QR; ++i)
     for (int e = tid; e < NB; e += NT) hist[i][e] = 0u;
   __syncthreads();
-  int b = sh_b, off = sh_off;
+  int b = __builtin_amdgcn_readfirstlane(sh_b), off = __builtin_amdgcn_readfirstlane(sh_off);
   uint32_t left = hi - lo;
 
   while (left > 0 && b < a.B) {
@@ -496,9 +523,12 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
       const int nvalid = pos[i] < 0 ? 0 : (min(pos[i] + 1, k1) + 3) & ~3;
       srs[i] = make_rsrc(a.S + ((size_t)b * a.qr + (pos[i] < 0 ? 0 : ri)) * a.ldS, (uint32_t)nvalid * 4u);
     }
-    const i32x4 krs = dma_rsrc(a.k + ((size_t)b * a.Lmax + k0) * ROW, (uint32_t)(k1 - k0) * ROW, kBufferFlags);
-    const i32x4 ksr = dma_rsrc(DT == kFP8 ? (const void*)(a.k_scale + (size_t)b * a.Lmax + k0) : (const void*)a.w,
-                               DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u, kBufferFlags);
+    i32x4 krs{}, ksr{};
+    if constexpr (!PAGED) {
+      krs = dma_rsrc(a.k + ((size_t)b * a.Lmax + k0) * ROW, (uint32_t)(k1 - k0) * ROW, kBufferFlags);
+      ksr = dma_rsrc(DT == kFP8 ? (const void*)(a.k_scale + (size_t)b * a.Lmax + k0) : (const void*)a.w,
+                     DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u, kBufferFlags);
+    }
 
     // the query registers are complete before the ring starts
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -507,16 +537,37 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
     // segment's pair 4 * (wid + W * (s / 4)) + s % 4; stage s % R holds it
     auto pair_of = [&](int s) { return G::BLOCK_PAIRS * (wid + W * (s / G::BLOCK_PAIRS)) + s % G::BLOCK_PAIRS; };
     auto issue = [&](const uint8_t* stage, int s) {
-      const int key0 = pair_of(s) * G::PAIR_KEYS;
+      int key0 = pair_of(s) * G::PAIR_KEYS;
+      i32x4 rk = krs, rs = ksr;
+      if constexpr (PAGED) {
+        // the pair's own descriptors: empty past the run's last key or for a
+        // page id outside the pool (the loads then write zeros)
+        const int p0 = k0 + key0;
+        const uint8_t* kb = a.k;
+        const float* sb = DT == kFP8 ? a.k_scale : a.w;
+        uint32_t nk = 0;
+        if (p0 < k1) {
+          const int pg = page_id(a.bt, (size_t)b * a.bt_stride + (p0 >> a.page_shift));
+          if ((unsigned)pg < (unsigned)a.num_pages) {
+            const size_t row = ((size_t)pg << a.page_shift) + (p0 & ((1 << a.page_shift) - 1));
+            kb += row * ROW;
+            if constexpr (DT == kFP8) sb += row;
+            nk = (uint32_t)min(G::PAIR_KEYS, k1 - p0);
+          }
+        }
+        rk = dma_rsrc(kb, nk * ROW, kBufferFlags);
+        rs = dma_rsrc(sb, DT == kFP8 ? nk * 4u : 0u, kBufferFlags);
+        key0 = 0;
+      }
       const uint32_t dst = lds_addr(stage);
 #pragma unroll
       for (int c = 0; c < G::LOADS; ++c) {
         const int slot = c * kWave + lane;
         const int kr = slot / G::CPR;
         const int chunk = (slot % G::CPR) ^ (kr & G::SWM);
-        lds_dma16(krs, dst + c * 1024, (uint32_t)((key0 + kr) * ROW + chunk * 16));
+        lds_dma16(rk, dst + c * 1024, (uint32_t)((key0 + kr) * ROW + chunk * 16));
       }
-      if constexpr (DT == kFP8) lds_dma4(ksr, dst + G::PAIR_BYTES, (uint32_t)((key0 + lane) * 4));
+      if constexpr (DT == kFP8) lds_dma4(rs, dst + G::PAIR_BYTES, (uint32_t)((key0 + lane) * 4));
     };
     // a stage is complete once at most the R-1 newer stages' loads (and
     // any score stores issued after it) are outstanding

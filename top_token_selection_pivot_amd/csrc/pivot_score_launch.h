@@ -31,26 +31,33 @@ static void refine_one(const RefineArgs& a, dim3 grid, int rows, hipStream_t st)
     hipLaunchKernelGGL((score_block_kernel<DT, D, HB, true, 8, RefineArgs>), grid, dim3(8 * kWave), 0, st, a);
 }
 // Decode scan workgroups are persistent: as many as fit on the chip at once.
-template <int DT, int D, int HB, int QR>
+template <int DT, int D, int HB, int QR, bool PAGED>
 static void decode_launch(const DecScanArgs& a, int zblocks, hipStream_t st) {
   using G = DecGeom<DT, D, QR>;
   static const int per_cu = [] {
     int nblk = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, decode_scan_kernel<DT, D, HB, QR>, G::THREADS, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, decode_scan_kernel<DT, D, HB, QR, PAGED>, G::THREADS,
+                                                     0) != hipSuccess ||
         nblk < 1)
       nblk = 1;
     return nblk;
   }();
   dim3 grid(device_cu_count() * per_cu, 1, zblocks);
-  hipLaunchKernelGGL((decode_scan_kernel<DT, D, HB, QR>), grid, dim3(G::THREADS), 0, st, a);
+  hipLaunchKernelGGL((decode_scan_kernel<DT, D, HB, QR, PAGED>), grid, dim3(G::THREADS), 0, st, a);
+}
+template <int DT, int D, int HB, bool PAGED>
+static void decode_qr(const DecScanArgs& a, int zblocks, hipStream_t st) {
+  if (a.qr == 1)
+    decode_launch<DT, D, HB, 1, PAGED>(a, zblocks, st);
+  else
+    decode_launch<DT, D, HB, 2, PAGED>(a, zblocks, st);
 }
 template <int DT, int D, int HB>
 static void decode_one(const DecScanArgs& a, int zblocks, hipStream_t st) {
-  if (a.qr == 1)
-    decode_launch<DT, D, HB, 1>(a, zblocks, st);
+  if (a.bt)
+    decode_qr<DT, D, HB, true>(a, zblocks, st);
   else
-    decode_launch<DT, D, HB, 2>(a, zblocks, st);
+    decode_qr<DT, D, HB, false>(a, zblocks, st);
 }
 
 // Calls f.operator()<D, HB>() for the supported head-dimension / head-block combination.
