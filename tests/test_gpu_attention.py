@@ -61,6 +61,23 @@ def test_attention_few_rows_chunked(Hq):
     _close(got, ref, "chunked")
 
 
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_attention_merge_over_many_chunks(Hq):
+    # 3 rows of 4100 slots: 33 chunks each, merged 16 at a time; row 1 has no
+    # valid slot in its first 2100 entries, row 2 none after its first 1000
+    print(f"case: sparse attention R=3 Hq={Hq} nidx=4100 (33 chunks)", flush=True)
+    rng = np.random.default_rng(100 + Hq)
+    L = 5000
+    q, k, v = _codes(rng, (3, Hq, 128)), _codes(rng, (L, 128)), _codes(rng, (L, 128))
+    idx = rng.integers(0, L, (3, 4100)).astype(np.int32)
+    idx[1, :2100] = -1
+    idx[2, 1000:] = -1
+    idx[2, 3000] = L + 7  # outside the sequence: skipped
+    got = pv.sparse_attention(_t(q), _t(k), _t(v), _t(idx)).cpu().numpy()
+    ref = oracle.sparse_attention(q, k, v, idx)
+    _close(got, ref, "33 chunks")
+
+
 def test_attention_many_rows_single_chunk():
     # many rows: one wave per row, no merge; causal rows like an indexer's output
     print("case: sparse attention R=1100 Hq=64 nidx=300 (one chunk per row)", flush=True)
@@ -100,6 +117,29 @@ def test_attention_large_scores_and_full_selection():
         ref = oracle.sparse_attention(q, k, v, idx, scale=scale)
         assert np.isfinite(got).all()
         _close(got, ref, f"scale {scale}")
+
+
+def test_attention_score_ramps():
+    # the score of position s is k_s[0] = 0.05 s, plus 20 from s = 1000 on:
+    # read in ascending order a head's maximum creeps up (several tiles pass
+    # before it has moved far enough to rescale) and jumps once; read in
+    # descending order the first tile holds the maximum
+    print("case: sparse attention, rising, falling and jumping score ramps", flush=True)
+    rng = np.random.default_rng(17)
+    L, Hq = 2048, 64
+    kf = rng.standard_normal((L, 128)).astype(np.float32)
+    kf[:, 0] = 0.05 * np.arange(L) + 20.0 * (np.arange(L) >= 1000)
+    qf = np.zeros((4, Hq, 128), np.float32)
+    qf[:, :, 0] = 1.0
+    qf[3, :, 0] = np.linspace(0.1, 1.0, Hq)  # a different slope per head
+    q, k, v = synth.encode_bf16(qf), synth.encode_bf16(kf), _codes(rng, (L, 128))
+    idx = np.stack([np.arange(L), np.arange(L)[::-1], rng.permutation(L), np.arange(L)]).astype(np.int32)
+    got = pv.sparse_attention(_t(q), _t(k), _t(v), _t(idx), scale=1.0).cpu().numpy()
+    ref = oracle.sparse_attention(q, k, v, idx, scale=1.0)
+    _close(got, ref, "ramps")
+    many = np.repeat(idx, 300, axis=0)  # 1200 rows: one chunk per row, no merge
+    got = pv.sparse_attention(_t(np.repeat(q, 300, axis=0)), _t(k), _t(v), _t(many), scale=1.0).cpu().numpy()
+    _close(got[::300], ref, "ramps, one chunk per row")
 
 
 def test_attention_after_the_indexer():

@@ -38,19 +38,34 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRangeFlags);
 }
 
-// bf16 code of x, round to nearest even (finite inputs)
-__device__ inline uint32_t bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// two floats as packed bf16 codes, round to nearest even (one conversion instruction)
+__device__ inline uint32_t bf16x2_rne(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){x0, x1}, bf16x2_t));
 }
 
-template <int HB>
-__global__ __launch_bounds__(kWave) void sattn_kernel(SAttnArgs a) {
+// The running maximum of a head moves only when a tile's maximum exceeds it by
+// more than kLazyMax (natural-log units), so the output is rarely rescaled;
+// the weights exp(x - m) then stay below e^kLazyMax.  The result is the same
+// in exact arithmetic: the output and the sum always refer to the same m.
+constexpr float kLazyMax = 8.f;
+
+// A workgroup holds NW = Hq / 32 waves on the same (chunk, row); wave w takes
+// heads 32 w .. 32 w + 31.  Each wave gathers the tile's key and value rows
+// itself (the second wave's gathers hit the cache the first one filled) and
+// keeps its registers under 256, so two waves share a SIMD and one wave's
+// gathers overlap the other's contractions and softmax.
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void sattn_kernel(SAttnArgs a) {
   constexpr int NKS = kAD / 16;   // k-steps of the score contraction
   constexpr int NDB = kADV / 32;  // 32-row blocks of value columns
-  __shared__ __attribute__((aligned(16))) uint16_t vs[32][kADV];  // the tile's value rows
+  __shared__ __attribute__((aligned(16))) uint16_t vs_all[NW][32][kADV];  // each wave's value tile
 
-  const int lane = threadIdx.x, n = lane & 31, hf = lane >> 5;
+  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  const int hb = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // head block of this wave
+  uint16_t(*vs)[kADV] = vs_all[hb];
   const int r = blockIdx.y, c = blockIdx.x;
   const int s0 = c * a.chunk, s1 = min(s0 + a.chunk, a.nidx);
   const size_t seq = (size_t)(r / a.rows_per_seq);
@@ -59,26 +74,18 @@ __global__ __launch_bounds__(kWave) void sattn_kernel(SAttnArgs a) {
   const __amdgpu_buffer_rsrc_t vr =
       rsrc(a.v + seq * (size_t)a.seq_stride * kADV, (uint32_t)a.seq_len * kADV * 2u);
   const int32_t* idx = a.idx + (size_t)r * a.nidx;
+  const int head = hb * 32 + n;
 
   // Q^T as the B operand: lane (head n, half hf) holds q[head][16 ks + 8 hf ..+8]
-  i32x4 qf[HB][NKS];
+  i32x4 qf[NKS];
 #pragma unroll
-  for (int nb = 0; nb < HB; ++nb)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[nb][ks] = *reinterpret_cast<const i32x4*>(a.q + ((size_t)r * a.Hq + nb * 32 + n) * kAD + 16 * ks + 8 * hf);
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = *reinterpret_cast<const i32x4*>(a.q + ((size_t)r * a.Hq + head) * kAD + 16 * ks + 8 * hf);
 
-  f32x16 o[NDB][HB];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int nb = 0; nb < HB; ++nb) o[db][nb] = f32x16{};
-  float m[HB], l[HB];
-#pragma unroll
-  for (int nb = 0; nb < HB; ++nb) {
-    m[nb] = -INFINITY;
-    l[nb] = 0.f;
-  }
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
 
   // the positions of the next tile are loaded one tile ahead
   int pos_next = s0 + n < s1 ? idx[s0 + n] : -1;
@@ -107,65 +114,58 @@ __global__ __launch_bounds__(kWave) void sattn_kernel(SAttnArgs a) {
     }
     pos_next = t0 + 32 + n < s1 ? idx[t0 + 32 + n] : -1;
     __builtin_amdgcn_sched_barrier(0);
-    // scores S^T (32 keys x 32 heads per head block)
-    f32x16 s[HB];
+    // scores S^T (32 keys x 32 heads)
+    f32x16 sc = f32x16{};
 #pragma unroll
-    for (int nb = 0; nb < HB; ++nb) {
-      s[nb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]),
-                                                        __builtin_bit_cast(bf16x8, qf[nb][ks]), s[nb], 0, 0, 0);
-    }
+    for (int ks = 0; ks < NKS; ++ks)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]),
+                                                   __builtin_bit_cast(bf16x8, qf[ks]), sc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int p = lane + 64 * i;
       *reinterpret_cast<u32x4*>(&vs[p >> 4][8 * (p & 15)]) = vv[i];
     }
-    // online softmax of head n (block nb): accumulator i holds key row
-    // 8 (i / 4) + 4 hf + i % 4 of the tile
-    i32x4 phi[HB][2], plo[HB][2];
+    // online softmax of head n: accumulator i holds key row 8 (i / 4) + 4 hf + i % 4
+    float mt = -INFINITY;
 #pragma unroll
-    for (int nb = 0; nb < HB; ++nb) {
-      float x[16];
-      float mt = -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+      sc[i] = ((vmask >> key) & 1u) ? sc[i] * a.scale : -INFINITY;
+      mt = fmaxf(mt, sc[i]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool grow = mt > m + kLazyMax;  // with m = -inf: any valid key
+    const float mn = grow ? mt : m;
+    const float alpha = grow ? __expf(m - mn) : 1.f;  // 0 on the first tile with a valid key
+    const float base = mn == -INFINITY ? 0.f : mn;
+    float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
-        x[i] = ((vmask >> key) & 1u) ? s[nb][i] * a.scale : -INFINITY;
-        mt = fmaxf(mt, x[i]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[nb], mt);
-      const float base = mn == -INFINITY ? 0.f : mn;
-      const float alpha = __expf(m[nb] - base);  // 0 while nothing was seen
-      float ls = 0.f;
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __expf(x[i] - base);
-        ls += p[i];
-      }
-      ls += __shfl_xor(ls, 32);
-      l[nb] = l[nb] * alpha + ls;
-      m[nb] = mn;
+    for (int i = 0; i < 16; ++i) {
+      sc[i] = __expf(sc[i] - base);
+      ls += sc[i];
+    }
+    ls += __shfl_xor(ls, 32);
+    l = l * alpha + ls;
+    // the output is zero until a head's first valid key, so only a lane whose
+    // maximum moved after that needs the rescale
+    if (__ballot(grow && m != -INFINITY)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][nb][i] *= alpha;
-      // P as the B operand of k-step ks2: elements j = 0..7 are accumulators 8 ks2 + j
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float a0 = p[8 * ks2 + 2 * w], a1 = p[8 * ks2 + 2 * w + 1];
-          const uint32_t h0 = bf16_rne(a0), h1 = bf16_rne(a1);
-          const uint32_t l0 = bf16_rne(a0 - __uint_as_float(h0 << 16));
-          const uint32_t l1 = bf16_rne(a1 - __uint_as_float(h1 << 16));
-          phi[nb][ks2][w] = (int)(h0 | (h1 << 16));
-          plo[nb][ks2][w] = (int)(l0 | (l1 << 16));
-        }
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
+    m = mn;
+    // P as the B operand of k-step ks2: elements j = 0..7 are accumulators 8 ks2 + j
+    i32x4 phi[2], plo[2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float a0 = sc[8 * ks2 + 2 * w], a1 = sc[8 * ks2 + 2 * w + 1];
+        const uint32_t h = bf16x2_rne(a0, a1);
+        phi[ks2][w] = (int)h;
+        plo[ks2][w] = (int)bf16x2_rne(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xFFFF0000u));
+      }
     // value tile written by every lane before it is read
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -186,13 +186,10 @@ __global__ __launch_bounds__(kWave) void sattn_kernel(SAttnArgs a) {
           const uint32_t e1 = vs[k0 + 8 * (j1 >> 2) + (j1 & 3)][col];
           af[w] = (int)(e0 | (e1 << 16));
         }
-#pragma unroll
-        for (int nb = 0; nb < HB; ++nb) {
-          o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
-                                                              __builtin_bit_cast(bf16x8, phi[nb][ks2]), o[db][nb], 0, 0, 0);
-          o[db][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
-                                                              __builtin_bit_cast(bf16x8, plo[nb][ks2]), o[db][nb], 0, 0, 0);
-        }
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
+                                                        __builtin_bit_cast(bf16x8, phi[ks2]), o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
+                                                        __builtin_bit_cast(bf16x8, plo[ks2]), o[db], 0, 0, 0);
       }
     // every lane has read the value tile before the next one is written
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -200,60 +197,91 @@ __global__ __launch_bounds__(kWave) void sattn_kernel(SAttnArgs a) {
   }
 
   // lane (head n, half hf) holds value columns 32 db + 8 (i / 4) + 4 hf + i % 4
+  if (a.nch == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* dst = a.out + ((size_t)r * a.Hq + head) * kADV;
 #pragma unroll
-  for (int nb = 0; nb < HB; ++nb) {
-    const int head = nb * 32 + n;
-    if (a.nch == 1) {
-      const float inv = l[nb] > 0.f ? 1.f / l[nb] : 0.f;
-      float* dst = a.out + ((size_t)r * a.Hq + head) * kADV;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = 32 * db + 8 * g4 + 4 * hf;
-          *reinterpret_cast<float4*>(dst + col) =
-              make_float4(o[db][nb][4 * g4] * inv, o[db][nb][4 * g4 + 1] * inv, o[db][nb][4 * g4 + 2] * inv,
-                          o[db][nb][4 * g4 + 3] * inv);
-        }
-    } else {
-      const size_t pc = (size_t)r * a.nch + c;
-      float* dst = a.part_o + (pc * a.Hq + head) * kADV;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = 32 * db + 8 * g4 + 4 * hf;
-          *reinterpret_cast<float4*>(dst + col) =
-              make_float4(o[db][nb][4 * g4], o[db][nb][4 * g4 + 1], o[db][nb][4 * g4 + 2], o[db][nb][4 * g4 + 3]);
-        }
-      if (hf == 0) {
-        a.part_ml[pc * 2 * a.Hq + head] = m[nb];
-        a.part_ml[pc * 2 * a.Hq + a.Hq + head] = l[nb];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = 32 * db + 8 * g4 + 4 * hf;
+        *reinterpret_cast<float4*>(dst + col) = make_float4(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv,
+                                                            o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
       }
+  } else {
+    const size_t pc = (size_t)r * a.nch + c;
+    float* dst = a.part_o + (pc * a.Hq + head) * kADV;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = 32 * db + 8 * g4 + 4 * hf;
+        *reinterpret_cast<float4*>(dst + col) =
+            make_float4(o[db][4 * g4], o[db][4 * g4 + 1], o[db][4 * g4 + 2], o[db][4 * g4 + 3]);
+      }
+    if (hf == 0) {
+      a.part_ml[pc * 2 * a.Hq + head] = m;
+      a.part_ml[pc * 2 * a.Hq + a.Hq + head] = l;
     }
   }
 }
 
 // Merges the chunks of one (row, head): with M the largest chunk maximum,
 // out = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c (zeros when the row
-// selected nothing).  One thread per value column; the chunk loop is unrolled
-// so that the chunks' loads are in flight together.
-__global__ __launch_bounds__(kADV) void sattn_combine_kernel(SAttnArgs a) {
-  const int r = blockIdx.y, h = blockIdx.x, col = threadIdx.x;
+// selected nothing).  A thread takes four value columns of one (row, head) and
+// up to kMergeChunks chunks at a time: every chunk's maximum, sum and partial
+// output are loaded before any is used (indices clamped, so no load is
+// conditional), which leaves one memory latency per round; a later round
+// rescales what the earlier ones accumulated.
+constexpr int kMergeChunks = 16;
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void sattn_combine_kernel(SAttnArgs a) {
+  const long long t = (long long)blockIdx.x * kMergeThreads + threadIdx.x;
+  const int q4 = (int)(t & 31);  // columns 4 q4 .. 4 q4 + 3
+  const long long rh = t >> 5;   // r * Hq + h
+  if (rh >= (long long)a.R * a.Hq) return;
+  const int r = (int)(rh / a.Hq), h = (int)(rh % a.Hq);
   const size_t p0 = (size_t)r * a.nch;
-  float M = -INFINITY;
-  for (int c = 0; c < a.nch; ++c) M = fmaxf(M, a.part_ml[(p0 + c) * 2 * a.Hq + h]);
-  float acc = 0.f, L = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 8
-    for (int c = 0; c < a.nch; ++c) {
-      const float* ml = a.part_ml + (p0 + c) * 2 * a.Hq;
-      const float wgt = __expf(ml[h] - M);
-      L += wgt * ml[a.Hq + h];
-      acc += wgt * a.part_o[((p0 + c) * a.Hq + h) * kADV + col];
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < a.nch; c0 += kMergeChunks) {
+    float mc[kMergeChunks], lc[kMergeChunks];
+    float4 oc[kMergeChunks];
+#pragma unroll
+    for (int i = 0; i < kMergeChunks; ++i) {
+      const size_t pc = p0 + min(c0 + i, a.nch - 1);
+      mc[i] = a.part_ml[pc * 2 * a.Hq + h];
+      lc[i] = a.part_ml[pc * 2 * a.Hq + a.Hq + h];
+      oc[i] = *reinterpret_cast<const float4*>(a.part_o + (pc * a.Hq + h) * kADV + 4 * q4);
     }
+    float Mn = M;
+#pragma unroll
+    for (int i = 0; i < kMergeChunks; ++i) {
+      if (c0 + i >= a.nch) mc[i] = -INFINITY;  // a clamped duplicate
+      Mn = fmaxf(Mn, mc[i]);
+    }
+    if (Mn == -INFINITY) continue;  // nothing selected so far
+    const float sc = __expf(M - Mn);  // 0 on the first round that sees a slot
+    L *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
+#pragma unroll
+    for (int i = 0; i < kMergeChunks; ++i) {
+      const float wgt = __expf(mc[i] - Mn);
+      L += wgt * lc[i];
+      acc.x += wgt * oc[i].x;
+      acc.y += wgt * oc[i].y;
+      acc.z += wgt * oc[i].z;
+      acc.w += wgt * oc[i].w;
+    }
+    M = Mn;
   }
-  a.out[((size_t)r * a.Hq + h) * kADV + col] = L > 0.f ? acc / L : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<float4*>(a.out + rh * kADV + 4 * q4) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 }  // namespace
@@ -266,10 +294,12 @@ hipError_t launch_sparse_attention(const SAttnArgs& a, hipStream_t st) {
   if (a.Hq == 32)
     hipLaunchKernelGGL(sattn_kernel<1>, grid, dim3(kWave), 0, st, a);
   else
-    hipLaunchKernelGGL(sattn_kernel<2>, grid, dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL(sattn_kernel<2>, grid, dim3(2 * kWave), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nch == 1) return e;
-  hipLaunchKernelGGL(sattn_combine_kernel, dim3(a.Hq, a.R), dim3(kADV), 0, st, a);
+  const long long threads = (long long)a.R * a.Hq * (kADV / 4);
+  hipLaunchKernelGGL(sattn_combine_kernel, dim3((unsigned)((threads + kMergeThreads - 1) / kMergeThreads)),
+                     dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 
