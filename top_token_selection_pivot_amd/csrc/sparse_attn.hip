@@ -38,6 +38,9 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRangeFlags);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
@@ -53,19 +56,27 @@ __device__ inline uint32_t bf16x2_rne(float x0, float x1) {
 constexpr float kLazyMax = 8.f;
 
 // A workgroup holds NW = Hq / 32 waves on the same (chunk, row); wave w takes
-// heads 32 w .. 32 w + 31.  Each wave gathers the tile's key and value rows
-// itself (the second wave's gathers hit the cache the first one filled) and
-// keeps its registers under 256, so two waves share a SIMD and one wave's
-// gathers overlap the other's contractions and softmax.
+// heads 32 w .. 32 w + 31.  With 64 heads a wave keeps its registers under
+// 256, so two waves share a SIMD and one's memory waits overlap the other's
+// work (a 32-head wave gathers alone and holds twice the pieces).  The
+// workgroup gathers each tile's key and value rows once, whole 256-byte rows
+// split over its waves, into LDS (double buffered, 16-byte chunks of row j
+// XOR-swizzled by j % 16 so that the fragment reads of 32 rows spread over
+// the banks); the next tile's rows are in flight in registers while the
+// current tile is computed, and one barrier per tile hands a tile over.
 template <int NW>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void sattn_kernel(SAttnArgs a) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW))) void sattn_kernel(SAttnArgs a) {
   constexpr int NKS = kAD / 16;   // k-steps of the score contraction
   constexpr int NDB = kADV / 32;  // 32-row blocks of value columns
-  __shared__ __attribute__((aligned(16))) uint16_t vs_all[NW][32][kADV];  // each wave's value tile
+  constexpr int ROWB = kAD * 2;   // bytes of a key row (= a value row)
+  constexpr int TILE = 32 * ROWB;
+  constexpr int PPL = 32 * (ROWB / 16) / (NW * kWave);  // 16-byte pieces per lane per tile and matrix
+  static_assert(kAD == kADV && PPL * NW * kWave == 32 * (ROWB / 16));
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t vt[2][TILE];
 
-  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-  const int hb = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // head block of this wave
-  uint16_t(*vs)[kADV] = vs_all[hb];
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hf = lane >> 5;
+  const int hb = __builtin_amdgcn_readfirstlane(tid >> 6);  // head block of this wave
   const int r = blockIdx.y, c = blockIdx.x;
   const int s0 = c * a.chunk, s1 = min(s0 + a.chunk, a.nidx);
   const size_t seq = (size_t)(r / a.rows_per_seq);
@@ -75,6 +86,12 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
       rsrc(a.v + seq * (size_t)a.seq_stride * kADV, (uint32_t)a.seq_len * kADV * 2u);
   const int32_t* idx = a.idx + (size_t)r * a.nidx;
   const int head = hb * 32 + n;
+  // byte offset of 16-byte chunk ch of row j in a tile
+  auto chunk_at = [](int j, int ch) { return j * ROWB + ((ch ^ (j & 15)) << 4); };
+  // this lane's row and column within a half k-step of the value tile for
+  // the transposing reads of V^T (see below)
+  const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // Q^T as the B operand: lane (head n, half hf) holds q[head][16 ks + 8 hf ..+8]
   i32x4 qf[NKS];
@@ -87,43 +104,41 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  // the positions of the next tile are loaded one tile ahead
-  int pos_next = s0 + n < s1 ? idx[s0 + n] : -1;
-  for (int t0 = s0; t0 < s1; t0 += 32) {
-    // this lane's key row (A operand row n) and its validity
-    const int pos = pos_next;
-    const bool valid = pos >= 0 && pos < a.seq_len;
-    const uint32_t vmask = (uint32_t)__ballot(valid);  // bit j: key row j of the tile is valid
-    // the tile's value rows go to LDS: piece p = lane + 64 i is 16 bytes of row p / 16
-    int rp[8];
+  // lane n (and n + 32) holds the position of slot n of the tile at t0
+  auto load_pos = [&](int t0) { return t0 + n < s1 ? idx[t0 + n] : -1; };
+  // piece p = tid + NW * 64 * i of a tile is chunk p % 16 of row p / 16
+  i32x4 gk[PPL], gv[PPL];
+  auto gather = [&](int posv) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rp[i] = __shfl(pos, (lane + 64 * i) >> 4);
-    // all of the tile's gathers are issued before any of them is used (the
-    // compiler would otherwise place each next to its use and wait for it)
-    i32x4 kf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      kf[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             kr, valid ? (pos * kAD + 16 * ks + 8 * hf) * 2 : 0x80000000u, 0, 0));
-    u32x4 vv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = lane + 64 * i, row = p >> 4, ch = p & 15;
-      const bool rv = (vmask >> row) & 1u;
-      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, rv ? (rp[i] * kADV + 8 * ch) * 2 : 0x80000000u, 0, 0);
+    for (int i = 0; i < PPL; ++i) {
+      const int p = tid + NW * kWave * i, j = p >> 4, ch = p & 15;
+      const int ps = __shfl(posv, j);
+      const bool ok = ps >= 0 && ps < a.seq_len;
+      gk[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            kr, ok ? (ps * kAD + 8 * ch) * 2 : 0x80000000u, 0, 0));
+      gv[i] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            vr, ok ? (ps * kADV + 8 * ch) * 2 : 0x80000000u, 0, 0));
     }
-    pos_next = t0 + 32 + n < s1 ? idx[t0 + 32 + n] : -1;
-    __builtin_amdgcn_sched_barrier(0);
-    // scores S^T (32 keys x 32 heads)
+  };
+  auto stash = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < PPL; ++i) {
+      const int p = tid + NW * kWave * i, j = p >> 4, ch = p & 15;
+      *reinterpret_cast<i32x4*>(&kt[b][chunk_at(j, ch)]) = gk[i];
+      *reinterpret_cast<i32x4*>(&vt[b][chunk_at(j, ch)]) = gv[i];
+    }
+  };
+
+  auto compute = [&](int b, int posv) {
+    const bool valid = posv >= 0 && posv < a.seq_len;
+    const uint32_t vmask = (uint32_t)__ballot(valid);  // bit j: key row j of the tile is valid
+    // scores S^T (32 keys x 32 heads): A fragment = elements 16 ks + 8 hf ..+8 of key row n
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[ks]),
+    for (int ks = 0; ks < NKS; ++ks) {
+      const i32x4 kf = *reinterpret_cast<const i32x4*>(&kt[b][chunk_at(n, 2 * ks + hf)]);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
                                                    __builtin_bit_cast(bf16x8, qf[ks]), sc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = lane + 64 * i;
-      *reinterpret_cast<u32x4*>(&vs[p >> 4][8 * (p & 15)]) = vv[i];
     }
     // online softmax of head n: accumulator i holds key row 8 (i / 4) + 4 hf + i % 4
     float mt = -INFINITY;
@@ -166,34 +181,45 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
         phi[ks2][w] = (int)h;
         plo[ks2][w] = (int)bf16x2_rne(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xFFFF0000u));
       }
-    // value tile written by every lane before it is read
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // O^T += V^T P: A fragment of k-step ks2 for value column 32 db + n holds the
-    // values of keys 16 ks2 + 8 (j / 4) + 4 hf + j % 4, j = 0..7
+    // values of keys 16 ks2 + 8 (j / 4) + 4 hf + j % 4, j = 0..7.  Each half
+    // (j = 0..3, j = 4..7) is one transposing LDS read: in every group of 16
+    // lanes, lane i names 4 consecutive values M_i[0..3] of a value row and
+    // lane j receives M_{4e + j/4}[j % 4], e = 0..3; so lane 16 G + i names
+    // row 4 (G / 2) + i / 4 of the half, columns 16 (G % 2) + 4 (i % 4) ..+3.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const int k0 = 16 * ks2 + 4 * hf, col = 32 * db + n;
-        i32x4 af;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int j0 = 2 * w, j1 = 2 * w + 1;
-          const uint32_t e0 = vs[k0 + 8 * (j0 >> 2) + (j0 & 3)][col];
-          const uint32_t e1 = vs[k0 + 8 * (j1 >> 2) + (j1 & 3)][col];
-          af[w] = (int)(e0 | (e1 << 16));
-        }
+        const int j0 = 16 * ks2 + tr_row, j1 = j0 + 8, col = 32 * db + tr_col;
+        const v4i16 e0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)&vt[b][chunk_at(j0, col >> 3) + (col & 7) * 2]);
+        const v4i16 e1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)&vt[b][chunk_at(j1, col >> 3) + (col & 7) * 2]);
+        const i32x4 af = __builtin_bit_cast(i32x4, (v8i16){e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]});
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
                                                         __builtin_bit_cast(bf16x8, phi[ks2]), o[db], 0, 0, 0);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
                                                         __builtin_bit_cast(bf16x8, plo[ks2]), o[db], 0, 0, 0);
       }
-    // every lane has read the value tile before the next one is written
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_wave_barrier();
+  };
+
+  // tile k's rows sit in buffer k % 2; tile k + 1's are in flight meanwhile
+  int pc = load_pos(s0), pn = load_pos(s0 + 32);
+  gather(pc);
+  stash(0);
+  gather(pn);
+  __syncthreads();
+  int b = 0;
+  for (int t0 = s0; t0 < s1; t0 += 32) {
+    const int pnn = load_pos(t0 + 64);
+    compute(b, pc);
+    stash(b ^ 1);  // every wave is done with that buffer since the last barrier
+    gather(pnn);
+    __syncthreads();
+    pc = pn;
+    pn = pnn;
+    b ^= 1;
   }
 
   // lane (head n, half hf) holds value columns 32 db + 8 (i / 4) + 4 hf + i % 4
@@ -209,8 +235,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
                                                             o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
       }
   } else {
-    const size_t pc = (size_t)r * a.nch + c;
-    float* dst = a.part_o + (pc * a.Hq + head) * kADV;
+    const size_t pc2 = (size_t)r * a.nch + c;
+    float* dst = a.part_o + (pc2 * a.Hq + head) * kADV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -220,8 +246,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2)))
             make_float4(o[db][4 * g4], o[db][4 * g4 + 1], o[db][4 * g4 + 2], o[db][4 * g4 + 3]);
       }
     if (hf == 0) {
-      a.part_ml[pc * 2 * a.Hq + head] = m;
-      a.part_ml[pc * 2 * a.Hq + a.Hq + head] = l;
+      a.part_ml[pc2 * 2 * a.Hq + head] = m;
+      a.part_ml[pc2 * 2 * a.Hq + a.Hq + head] = l;
     }
   }
 }
