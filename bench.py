@@ -11,8 +11,10 @@ in HBM.  Prints one JSON line:
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
 
 plus context measured in the same run: speedup over the dense indexer (g=1)
-on the same GPU, Refine/dense top-k overlap, the g sweep, PIVOT-Reuse and the
-MTP decode step (B=32, fp8, µs per step).
+on the same GPU, Refine/dense top-k overlap, the g sweep, PIVOT-Reuse, the
+sliding window, several sequences in one call, the 16K bf16 and 64K fp8 prefill
+workloads (with their scan's rate against the bf16 or fp8 matrix peak), the
+MTP decode step (B=32, fp8, µs per step) and sparse main attention.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3]
 """
@@ -32,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E peak
 
 
@@ -176,6 +179,42 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
     log(f"decode {dsec*1e6:.1f} us/step; scan {key_bytes/(scan_ms_d/1e3)/1e9:.0f} GB/s; "
         f"g=4 {g4_sec*1e6:.1f} us/step; paged (64) {paged_sec*1e6:.1f} us/step, "
         f"scan {pscan_ms*1e3:.1f} us")
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_prefill(torch, pv, d, L, modes, peak, g=8, topk=2048, C=4096, steps=5):
+    """ms per call and queries/s of one prefill workload (g=8 groups; dense is
+    g=1), and the full-prefix scan's matrix-core rate from the library's
+    per-launch events against `peak` (the code type's dense peak)."""
+    H, D = d["q"].shape[1], d["q"].shape[2]
+    fp8 = d.get("q_scale") is not None
+    res = {"L": L, "H": H, "D": D, "dtype": "fp8" if fp8 else "bf16", "g": g, "topk": topk, "C": C}
+    out = torch.empty((L, topk), dtype=torch.int32, device="cuda")
+    for mode in modes:
+        gg, cc = (1, topk) if mode == "dense" else (g, C)
+        ws = torch.empty(pv.workspace_size(L, H, D, gg, topk, cc, mode, 1 if fp8 else 0),
+                         dtype=torch.uint8, device="cuda")
+        f = lambda: pv.indexer(d["q"], d["w"], d["k"], g=gg, topk=topk, C=cc, mode=mode, out=out,
+                               workspace=ws, q_scale=d.get("q_scale"), k_scale=d.get("k_scale"))
+        s = time_steps(f, steps, 1, torch)
+        pv.profile_enable(True)
+        pv.profile_read()
+        f()
+        torch.cuda.synchronize()
+        prof = pv.profile_read()
+        pv.profile_enable(False)
+        scan_tf = 2.0 * H * D * proxy_scan_pairs(L, gg) / (prof["scan"][0] / 1e3) / 1e12
+        res[mode] = {"ms_per_call": s * 1e3, "queries_per_s": L / s, "scan_TFLOPs": scan_tf,
+                     "scan_frac_of_peak": scan_tf / peak,
+                     "kernels_ms": {k: v[0] for k, v in prof.items() if v[1]}}
+        del ws
+    if "dense" in res:
+        for mode in modes:
+            if mode != "dense":
+                res[mode]["speedup_vs_dense"] = res["dense"]["ms_per_call"] / res[mode]["ms_per_call"]
+    log(f"prefill L={L} {res['dtype']}: " + ", ".join(f"{m} {res[m]['ms_per_call']:.2f} ms" for m in modes))
+    del out
     torch.cuda.empty_cache()
     return res
 
@@ -488,7 +527,19 @@ def main():
                                                    mode="refine", out=out_v), 5, 2, torch)
         extras["varlen_refine_g8"] = {"lengths": lens, "ms_per_call": s_v * 1e3,
                                       "queries_per_s": 16384 / s_v}
-        del dv_, out_v
+        del out_v
+        # the other prefill workloads, one sequence each: 16K bf16 (dense,
+        # Reuse, Refine) and 64K fp8 (Reuse, Refine)
+        other = {"dsa_prefill_16k": measure_prefill(torch, pv, dv_, 16384, ("dense", "reuse", "refine"),
+                                                    BF16_PEAK_TFLOPS)}
+        del dv_
+        torch.cuda.empty_cache()
+        log("generating the 64K fp8 prefill inputs")
+        d8 = upload(synth.make("long_prefill_fp8_64k"), torch)
+        other["long_prefill_fp8_64k"] = measure_prefill(torch, pv, d8, 65536, ("reuse", "refine"),
+                                                        FP8_PEAK_TFLOPS)
+        extras["other_prefill_workloads"] = other
+        del d8
         torch.cuda.empty_cache()
         extras["decode"] = measure_decode(torch, pv, synth, 200, 100)
         extras["sparse_attention"] = measure_attention(torch, pv, synth)

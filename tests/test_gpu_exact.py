@@ -130,19 +130,27 @@ def test_tiny_proxy_bits_and_candidates(tiny):
         assert np.array_equal(cand, ref)
 
 
-def test_fp8_proxy_bits():
-    print("case: fp8 proxy bits (float inputs, partial last group)", flush=True)
-    inp = synth.dsa_prefill(L=203, H=64, D=128, dtype="fp8", seed=77)
-    d = to_device(inp)
-    v = oracle.View.of(inp)
-    for g in (8, 2, 1):
-        qbar, qs, wbar = pv.proxy_mean(d["q"], d["w"], g, q_scale=d["q_scale"])
-        qbar, qs, wbar = qbar.cpu().numpy(), qs.cpu().numpy(), wbar.cpu().numpy()
-        for j in range((203 + g - 1) // g):
-            n = min(g, 203 - j * g)
-            c, s, wb = oracle.proxy(v, j * g, n)
-            assert np.array_equal(qbar[j], c), (g, j)
-            assert qs[j] == s and np.array_equal(wbar[j], wb), (g, j)
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_float_proxy_bits(dtype):
+    # a short sequence (every group checked) and a longer one (sampled groups)
+    for L, gs, every in ((203, (8, 2, 1), 1), (2100, (8, 2), 29)):
+        print(f"case: {dtype} proxy bits (float inputs, partial last group) L={L}", flush=True)
+        inp = synth.dsa_prefill(L=L, H=64, D=128, dtype=dtype, seed=77)
+        d = to_device(inp)
+        v = oracle.View.of(inp)
+        for g in gs:
+            qbar, qs, wbar = pv.proxy_mean(d["q"], d["w"], g, q_scale=d.get("q_scale"))
+            if dtype == "bf16":
+                qbar = qbar.view(torch.int16)
+            qbar, qs, wbar = qbar.cpu().numpy(), qs.cpu().numpy(), wbar.cpu().numpy()
+            if dtype == "bf16":
+                qbar = qbar.view(np.uint16)
+            G = (L + g - 1) // g
+            for j in sorted(set(range(0, G, every)) | {G - 1}):
+                n = min(g, L - j * g)
+                c, s, wb = oracle.proxy(v, j * g, n)
+                assert np.array_equal(qbar[j], c), (g, j)
+                assert qs[j] == s and np.array_equal(wbar[j], wb), (g, j)
 
 
 SHAPES = [  # (L, H, D, g, topk, C, dtype)
