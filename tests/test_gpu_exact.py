@@ -223,6 +223,31 @@ def test_long_exact_sampled_groups():
         assert np.array_equal(out[j * g:(j + 1) * g], ref), j
 
 
+@pytest.mark.parametrize("kmax", [4, 0])
+def test_long_rows_selection(kmax):
+    # rows of 30720 scores or more are sampled before their first pass; with
+    # spread-out integer scores the sampled estimate lets one pass gather the
+    # candidates, with all-zero keys (every score equal) it cannot and the
+    # selection falls back to passes over the row: both must be exact
+    print(f"case: L=40000 H=8 D=64 integer inputs, kmax={kmax}, long-row top-k", flush=True)
+    L, g, topk, C = 40000, 8, 2048, 4096
+    inp = synth.small_integer(L, 8, 64, seed=41, qmax=4, kmax=kmax, wmax=3)
+    v = oracle.View.of(inp)
+    G = L // g
+    rng = np.random.default_rng(9)
+    out = _run(inp, "refine", g, topk, C)
+    cand = pv.candidates(*(to_device(inp)[x] for x in ("q", "w", "k")), g=g, topk=topk, C=C,
+                         mode="refine").cpu().numpy()
+    groups = sorted({0, 3839, 3840, G - 2, G - 1} | set(rng.integers(3840, G, 6).tolist()))
+    for j in groups:
+        ref, rc, _ = oracle.group(v, j * g, j * g, g, topk, C, "refine")
+        assert np.array_equal(cand[j], rc), j
+        assert np.array_equal(out[j * g:(j + 1) * g], ref), j
+    dense = _run(inp, "dense", 1, topk, topk)
+    rows = np.array(sorted({30719, 30720, L - 1} | set(rng.integers(30720, L, 5).tolist())))
+    assert np.array_equal(dense[rows], oracle.dense_rows(v, rows, topk))
+
+
 def test_deterministic_repeat():
     print("case: repeated calls are identical", flush=True)
     inp = synth.dsa_prefill(L=4096, H=64, D=128, seed=12)

@@ -200,15 +200,19 @@ hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st) {
 // histograms its top 12 bits.  Every key at or above the threshold bin is then
 // gathered into LDS in index order (a row that fits is staged whole during
 // pass 1); the remaining 20 bits and the emission run on that LDS copy, so a
-// row is read from memory at most twice.  If the threshold bin is too crowded
-// for LDS (e.g. a huge run of equal scores), the selection falls back to
-// further passes over the row in memory.
+// row is read from memory at most twice.  A long row is read about once: a
+// sixteenth of it is sampled first, and pass 1 gathers the keys at or above a
+// conservative bin estimated from the sample while it histograms (pass 2 is
+// needed only when the estimate turns out too high or too low).  If the
+// threshold bin is too crowded for LDS (e.g. a huge run of equal scores), the
+// selection falls back to further passes over the row in memory.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkCap = kSelectCap;  // keys staged in LDS
 constexpr int kTopkBits1 = 12;        // first digit: bits 31..20
 static_assert((1 << kTopkBits1) == kSelectBins1, "first-digit histogram width");
 constexpr int kTopkU = 4;          // 16-byte loads in flight per thread
+constexpr int kTopkSampleMin = 4 * kTopkCap;  // rows this long are sampled first
 
 __device__ inline int ref_count(const int32_t* list, int m, int t) {
   // number of leading entries of the ascending, -1 padded list that are in [0, t]
@@ -502,8 +506,78 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
 
   // ---- pass 1: histogram of the top 12 bits (rows that fit are staged in LDS)
   const bool whole = n <= kTopkCap;
+  // A long row is first sampled (the first 64 scores of every 1024): the bin
+  // holding a conservative rank of the sample, b_est, is at or below the
+  // row's threshold bin unless the sample is far off.  Pass 1 then histograms
+  // and gathers into LDS, in index order, only the keys whose first digit is
+  // >= b_est.  With at least m of them the threshold bin b1 is >= b_est and
+  // the histogram of those bins finds it; if they also fit, the row has been
+  // read once, else pass 2 gathers from the row.  With fewer than m the
+  // whole row is histogrammed again.
+  const bool est = !whole && n >= kTopkSampleMin;
+  uint32_t b_est = NB1;
   __syncthreads();
-  for (int base = 0; base < n; base += kTopkU * NT * 4) {
+  if (est) {
+    const int nch = n >> 10;  // whole chunks of 1024 scores
+    for (int i = tid; i < nch * 16; i += NT) {
+      const float4 s4 = *reinterpret_cast<const float4*>(row + ((i >> 4) << 10) + ((i & 15) << 2));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&sm.hist[score_key(f4(s4, e)) >> (32 - kTopkBits1)], 1u);
+    }
+    __syncthreads();
+    const uint32_t ns = (uint32_t)nch * 64u;
+    const float r = (float)m * (float)ns / (float)n;  // the threshold's expected rank in the sample
+    const uint32_t rank = (uint32_t)(r + 3.f * sqrtf(r)) + 2u;
+    b_est = 0u;
+    if (rank <= ns) {
+      find_bin<NT>(sm.hist, NB1, rank, sm.scratch, &sm.sh_bin, &sm.sh_above);
+      b_est = sm.sh_bin;
+    }
+    for (int b = tid; b < NB1; b += NT) sm.hist[b] = 0u;
+    __syncthreads();
+  }
+  uint32_t gathered = 0;  // keys with first digit >= b_est (staged while they fit)
+  if (est) {
+    constexpr int E = 4 * kTopkU;
+    for (int base = 0; base < n; base += E * NT) {
+      const int s0 = base + tid * E;
+      float4 v4[kTopkU];
+#pragma unroll
+      for (int u = 0; u < kTopkU; ++u) v4[u] = load4(row, s0 + 4 * u, n);
+      uint32_t key[E];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        key[e] = score_key(f4(v4[e >> 2], e & 3));
+        if (s0 + e < n && (key[e] >> (32 - kTopkBits1)) >= b_est) {
+          atomicAdd(&sm.hist[key[e] >> (32 - kTopkBits1)], 1u);
+          ++cnt;
+        }
+      }
+      uint32_t tot;
+      uint32_t p = gathered + block_exclusive_sum<NT>(cnt, sm.scratch, &tot);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (s0 + e < n && (key[e] >> (32 - kTopkBits1)) >= b_est) {
+          if (p < (uint32_t)kTopkCap) {
+            sm.ckey[p] = key[e];
+            sm.cslot[p] = s0 + e;
+          }
+          ++p;
+        }
+      }
+      gathered += tot;
+    }
+  }
+  // the full first-digit histogram: rows that were not sampled, and sampled
+  // rows whose estimate was above the threshold bin
+  const bool full = !est || gathered < m;
+  if (est && full) {
+    __syncthreads();
+    for (int b = tid; b < NB1; b += NT) sm.hist[b] = 0u;
+    __syncthreads();
+  }
+  for (int base = 0; full && base < n; base += kTopkU * NT * 4) {
     if (!(whole_pre && base == 0)) {
 #pragma unroll
       for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
@@ -533,6 +607,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   int ncand;
   if (whole) {
     ncand = n;
+  } else if (!full && gathered <= (uint32_t)kTopkCap) {
+    ncand = (int)gathered;  // every key of bins >= b1 (>= b_est) is staged, in index order
   } else if (cand_total <= (uint32_t)kTopkCap) {
     // ---- pass 2: gather every key with first digit >= b1 into LDS, in index order
     constexpr int E = 4 * kTopkU;
