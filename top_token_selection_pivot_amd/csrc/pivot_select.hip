@@ -538,12 +538,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   }
   uint32_t gathered = 0;  // keys with first digit >= b_est (staged while they fit)
   if (est) {
+    // rounds of 16 consecutive scores per thread; the next round's loads are
+    // in flight during this round's block scan
     constexpr int E = 4 * kTopkU;
+    float4 nx[kTopkU];
+#pragma unroll
+    for (int u = 0; u < kTopkU; ++u) nx[u] = load4(row, tid * E + 4 * u, n);
     for (int base = 0; base < n; base += E * NT) {
       const int s0 = base + tid * E;
       float4 v4[kTopkU];
 #pragma unroll
-      for (int u = 0; u < kTopkU; ++u) v4[u] = load4(row, s0 + 4 * u, n);
+      for (int u = 0; u < kTopkU; ++u) v4[u] = nx[u];
+      if (base + E * NT < n) {
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) nx[u] = load4(row, s0 + E * NT + 4 * u, n);
+      }
       uint32_t key[E];
       uint32_t cnt = 0;
 #pragma unroll
@@ -613,11 +622,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     // ---- pass 2: gather every key with first digit >= b1 into LDS, in index order
     constexpr int E = 4 * kTopkU;
     uint32_t running = 0;
+    float4 nx[kTopkU];
+#pragma unroll
+    for (int u = 0; u < kTopkU; ++u) nx[u] = load4(row, tid * E + 4 * u, n);
     for (int base = 0; base < n; base += E * NT) {
       const int s0 = base + tid * E;
       float4 v[kTopkU];
 #pragma unroll
-      for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, s0 + 4 * u, n);
+      for (int u = 0; u < kTopkU; ++u) v[u] = nx[u];
+      if (base + E * NT < n) {
+#pragma unroll
+        for (int u = 0; u < kTopkU; ++u) nx[u] = load4(row, s0 + E * NT + 4 * u, n);
+      }
       uint32_t key[E];
       uint32_t cnt = 0;
 #pragma unroll
