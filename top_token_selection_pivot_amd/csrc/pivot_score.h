@@ -507,31 +507,12 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
     float qs[QR];
     int pos[QR];
     __amdgpu_buffer_rsrc_t srs[QR];
-#pragma unroll
-    for (int i = 0; i < QR; ++i) {
-      const int ri = ri0 + i;
-      pos[i] = -1;
-      qs[i] = 1.f;
-      if (ri < a.qr) {
-        const size_t rowi = (size_t)b * a.qr + ri;
-        q[i].load(a.q + rowi * a.H * ROW, a.w + rowi * a.H, a.H, lane);
-        if constexpr (DT == kFP8) qs[i] = a.q_scale[rowi];
-        pos[i] = (a.qr == 1 ? nb - 1 : nb - a.g + ri) - a.excl;
-      }
-      // whole 16-byte pieces (the row stride is a multiple of 64 keys): the
-      // up-to-3 scores past the causal limit that this lets through are unused
-      const int nvalid = pos[i] < 0 ? 0 : (min(pos[i] + 1, k1) + 3) & ~3;
-      srs[i] = make_rsrc(a.S + ((size_t)b * a.qr + (pos[i] < 0 ? 0 : ri)) * a.ldS, (uint32_t)nvalid * 4u);
-    }
     i32x4 krs{}, ksr{};
     if constexpr (!PAGED) {
       krs = dma_rsrc(a.k + ((size_t)b * a.Lmax + k0) * ROW, (uint32_t)(k1 - k0) * ROW, kBufferFlags);
       ksr = dma_rsrc(DT == kFP8 ? (const void*)(a.k_scale + (size_t)b * a.Lmax + k0) : (const void*)a.w,
                      DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u, kBufferFlags);
     }
-
-    // the query registers are complete before the ring starts
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // wave-local pair s is pair s % 4 of the wave's block s / 4, i.e. the
     // segment's pair 4 * (wid + W * (s / 4)) + s % 4; stage s % R holds it
@@ -610,9 +591,30 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
     // whole blocks per wave; loads past the segment's last pair read zeros
     const int nblk = (np + G::BLOCK_PAIRS - 1) / G::BLOCK_PAIRS;
     const int npw = nblk > wid ? G::BLOCK_PAIRS * ((nblk - wid + W - 1) / W) : 0;
+    // the ring starts filling before the query rows are loaded, so that the
+    // two latencies overlap
     issue(ring0[wid], 0);
     issue(ring1[wid], 1);
     if constexpr (R > 2) issue(ring2[wid], 2);
+#pragma unroll
+    for (int i = 0; i < QR; ++i) {
+      const int ri = ri0 + i;
+      pos[i] = -1;
+      qs[i] = 1.f;
+      if (ri < a.qr) {
+        const size_t rowi = (size_t)b * a.qr + ri;
+        q[i].load(a.q + rowi * a.H * ROW, a.w + rowi * a.H, a.H, lane);
+        if constexpr (DT == kFP8) qs[i] = a.q_scale[rowi];
+        pos[i] = (a.qr == 1 ? nb - 1 : nb - a.g + ri) - a.excl;
+      }
+      // whole 16-byte pieces (the row stride is a multiple of 64 keys): the
+      // up-to-3 scores past the causal limit that this lets through are unused
+      const int nvalid = pos[i] < 0 ? 0 : (min(pos[i] + 1, k1) + 3) & ~3;
+      srs[i] = make_rsrc(a.S + ((size_t)b * a.qr + (pos[i] < 0 ? 0 : ri)) * a.ldS, (uint32_t)nvalid * 4u);
+    }
+    // the query registers are complete (and with them the ring's first
+    // stages) before the first contraction
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     for (int s = 0; s < npw; s += R) {
       lds_dma_wait<(R - 1) * kStageOps>();
       compute(ring0[wid], s);
