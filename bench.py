@@ -17,6 +17,7 @@ workloads (with their scan's rate against the bf16 or fp8 matrix peak), the
 MTP decode step (B=32, fp8, µs per step) and sparse main attention.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+    python bench.py --decode-only | --fp8-only | --attention-only   (one part alone)
 """
 from __future__ import annotations
 
@@ -56,6 +57,8 @@ def parse():
                     help="first run 3 plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the MTP decode step (used under a profiler)")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only the 64K fp8 prefill workload (Reuse, Refine)")
     ap.add_argument("--attention-only", action="store_true",
                     help="time only the sparse main attention after the indexer")
     return ap.parse_args()
@@ -372,6 +375,14 @@ def main():
                           "value": res["us_per_step"], "unit": "us/step", "n_gpus": 1,
                           "steps": args.steps, "higher_is_better": False, "decode": res}),
               flush=True)
+        return
+    if args.fp8_only:
+        log("generating the 64K fp8 prefill inputs")
+        d8 = upload(synth.make("long_prefill_fp8_64k"), torch)
+        res = measure_prefill(torch, pv, d8, 65536, ("reuse", "refine"), FP8_PEAK_TFLOPS,
+                              steps=args.steps)
+        print(json.dumps({"metric": "64K fp8 prefill ms/call (g=8)", "n_gpus": 1,
+                          "long_prefill_fp8_64k": res}), flush=True)
         return
     if args.attention_only:
         res = measure_attention(torch, pv, synth)
