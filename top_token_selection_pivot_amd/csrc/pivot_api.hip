@@ -29,7 +29,7 @@ int fail(int status, const char* fmt, ...) {
 
 constexpr size_t kAlign = 256;
 constexpr int kScanRowsPerLaunch = 1024;          // scan rows per launch within a pass
-constexpr size_t kScoreBudget = size_t(1) << 30;  // preferred score bytes per pass
+constexpr size_t kScoreBudget = size_t(2) << 30;  // preferred score bytes per pass
 constexpr int kScanKeyChunk = 2048;              // keys per scan workgroup
 constexpr int kRefineSlotChunk = 1024;           // candidate slots per refine workgroup
 
