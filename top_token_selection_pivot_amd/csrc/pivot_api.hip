@@ -315,7 +315,7 @@ struct DecodePlan {
   int parts;  // workgroups per row in the decode top-m gather
   long long ldS, ldR;
   size_t off_qbar, off_qs, off_wbar, off_cand, off_S, off_R, off_hist, off_ckey, off_cslot, off_ccount,
-      total;
+      off_thr, total;
 };
 
 DecodePlan plan_decode(int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
@@ -348,6 +348,8 @@ DecodePlan plan_decode(int B, int Lmax, int H, int D, int g, int topk, int C, in
   off = align_up(off + (size_t)p.rows * p.parts * kSelectCap * 4);
   p.off_ccount = off;
   off = align_up(off + (size_t)p.rows * p.parts * 4);
+  p.off_thr = off;
+  off = align_up(off + (size_t)p.rows * 2 * 4);
   p.total = off;
   return p;
 }
@@ -556,6 +558,7 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   DecSelectArgs sel{S, p.ldS, p.rows, 0, 0, g, Lmax, cache_len, hist, p.parts,
                     (uint32_t*)(ws + p.off_ckey), (int32_t*)(ws + p.off_cslot), (int32_t*)(ws + p.off_ccount),
                     nullptr, 0, excl};
+  sel.thr = (uint32_t*)(ws + p.off_thr);
   const WindowArgs wa{out, ldo, B * g, topk, window, 1, g, Lmax, cache_len, 0};
   if (mode == PIVOT_MODE_DENSE) {
     PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_fill_u32(hist, (size_t)p.rows * kSelectBins1, 0u, s),

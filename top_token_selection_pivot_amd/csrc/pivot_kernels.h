@@ -99,8 +99,9 @@ struct DecScanArgs {
 // Top-m of decode score rows with precomputed first-digit histograms: `parts`
 // workgroups per row gather the keys at or above the threshold bin of their
 // slice into per-slice regions ([nrows][parts][kTopkCap] keys and slots,
-// counts [nrows][parts], -1 if the threshold bin is too crowded), then one
-// workgroup per row finishes the selection.
+// counts [nrows][parts], -1 if the threshold bin is too crowded), the first
+// of them also storing the row's threshold bin and the count of keys above it
+// in `thr` ([nrows][2]), then one workgroup per row finishes the selection.
 struct DecSelectArgs {
   const float* S;
   long long ldS;
@@ -116,6 +117,7 @@ struct DecSelectArgs {
   int32_t* out;
   long long ldo;
   int excl = 0;  // window excluded: row lengths shrink by excl
+  uint32_t* thr = nullptr;  // per row: first-digit threshold bin, keys in higher bins
 };
 
 // Row-length rules of the top-m selection.

@@ -898,8 +898,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 // of every row, so the threshold bin is known up front and a row can be split
 // across workgroups.  Gather: each of `parts` workgroups compacts, in index
 // order, the keys of its slice whose first digit is at or above the threshold
-// bin.  Finalize: one workgroup per row concatenates the slices in LDS (they
-// hold at most kTopkCap keys in total) and finishes the radix select; a
+// bin (the row's first gather workgroup also stores that bin for the
+// finalize).  Finalize: one workgroup per row concatenates the slices in LDS
+// (they hold at most kTopkCap keys in total) and finishes the radix select; a
 // crowded threshold bin (any slice count -1) falls back to passes over the row.
 // ---------------------------------------------------------------------------
 constexpr int kGatherThreads = 256;
@@ -952,6 +953,10 @@ __global__ __launch_bounds__(kGatherThreads) void dec_gather_kernel(DecSelectArg
   find_bin_global<NT>(h, m, scratch, &sh_bin, &sh_above);
   const uint32_t b1 = sh_bin;
   const uint32_t cand_total = sh_above + h[b1];
+  if (p == 0 && tid == 0) {  // the finalize takes the threshold bin from here
+    a.thr[2 * i] = b1;
+    a.thr[2 * i + 1] = sh_above;
+  }
   int32_t* cnt_out = a.ccount + (size_t)i * a.parts + p;
   if (cand_total > (uint32_t)kTopkCap) {
     if (tid == 0) *cnt_out = -1;
@@ -995,13 +1000,11 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
   __shared__ SelectShared sm;
   __shared__ int sh_bad;
   const int i = blockIdx.x, tid = threadIdx.x;
-  // the row length, the row's histogram and the slice counts are loaded together
-  const uint32_t* h = a.hist + (size_t)i * kSelectBins1;
+  // the row length, the threshold bin found by the gather and the slice
+  // counts are loaded together
   const int32_t* cnt = a.ccount + (size_t)i * a.parts;
-  uint32_t hv[kSelectBins1 / NT];
-#pragma unroll
-  for (int e = 0; e < kSelectBins1 / NT; ++e) hv[e] = h[tid + e * NT];
   const int c_own = tid < a.parts ? cnt[tid] : 0;
+  const uint32_t b1 = a.thr[2 * i], above = a.thr[2 * i + 1];
   const int n = decode_row_length(a, i);
   const uint32_t m = (uint32_t)a.m;
   const float* row = a.S + (long long)i * a.ldS;
@@ -1010,14 +1013,11 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
     for (int s = tid; s < (int)m; s += NT) out[s] = s < n ? s : -1;
     return;
   }
-#pragma unroll
-  for (int e = 0; e < kSelectBins1 / NT; ++e) sm.hist[tid + e * NT] = hv[e];
   if (tid == 0) sh_bad = 0;
   __syncthreads();
   if (c_own < 0) sh_bad = 1;
-  find_bin<NT>(sm.hist, kSelectBins1, m, sm.scratch, &sm.sh_bin, &sm.sh_above);
-  const uint32_t b1 = sm.sh_bin;
-  const uint32_t rem = m - sm.sh_above;
+  __syncthreads();
+  const uint32_t rem = m - above;
   if (sh_bad) {
     select_finish(sm, -1, b1, rem, row, n, m, nullptr, out);
     return;
