@@ -249,11 +249,22 @@ def test_long_rows_selection(kmax):
 
 
 def test_deterministic_repeat():
-    print("case: repeated calls are identical", flush=True)
-    inp = synth.dsa_prefill(L=4096, H=64, D=128, seed=12)
-    a = _run(inp, "refine", 8, 256, 512)
-    b = _run(inp, "refine", 8, 256, 512)
-    assert np.array_equal(a, b)
+    # float inputs (where a different summation order would show), ten calls
+    # each: a prefill whose long rows take the sampled top-k, and a decode step
+    print("case: repeated calls are identical (prefill L=40000, decode B=8)", flush=True)
+    inp = synth.dsa_prefill(L=40000, H=64, D=128, seed=12)
+    d = to_device(inp)
+    ws = torch.empty(pv.workspace_size(40000, 64, 128, 8, 256, 512, "refine", 0), dtype=torch.uint8,
+                     device="cuda")
+    runs = [pv.indexer(d["q"], d["w"], d["k"], g=8, topk=256, C=512, mode="refine",
+                       workspace=ws).cpu().numpy() for _ in range(10)]
+    assert all(np.array_equal(runs[0], r) for r in runs[1:])
+    dec = synth.decode_mtp(B=8, Lmin=4000, Lmax=40000, H=64, D=128, g=2, seed=77)
+    dd = to_device(dec)
+    outs = [pv.indexer_decode(dd["q"], dd["w"], dd["k"], dd["cache_len"], topk=256, C=512,
+                              mode="refine", q_scale=dd["q_scale"], k_scale=dd["k_scale"]).cpu().numpy()
+            for _ in range(10)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
 def _decode_inputs(B, lens, g, H=8, D=64, dtype="bf16", Lmax=None, seed=3):
