@@ -1,7 +1,8 @@
 """GPU parity of several prefill sequences in one call (variable lengths, one
 after another in the inputs): every sequence's rows must equal the oracle's for
 that sequence alone (integer-valued inputs: bit for bit), in every mode, with
-and without a sliding window, including empty and one-token sequences."""
+and without a sliding window, for bf16 and fp8 codes (per-token scales), including
+empty and one-token sequences."""
 import numpy as np
 import pytest
 import torch
@@ -62,3 +63,29 @@ def test_varlen_equals_separate_calls(batch):
         one = pv.indexer(d["q"][a:b].contiguous(), d["w"][a:b].contiguous(), d["k"][a:b].contiguous(),
                          g=4, topk=24, C=60, mode="refine")
         assert torch.equal(got[a:b], one), i
+
+
+LENS8 = [129, 0, 1, 1000, 3, 260]
+
+
+@pytest.mark.parametrize("mode", ["dense", "reuse", "refine"])
+def test_varlen_fp8_bit_exact(mode):
+    # fp8 codes of small integers with unit scales: every sum is exact, so the
+    # packed call must reproduce each sequence's oracle rows bit for bit
+    print(f"case: varlen fp8 prefill lengths {LENS8} g=8 k=32 C=96 {mode}", flush=True)
+    inp = synth.small_integer(sum(LENS8), 8, 64, seed=91, qmax=2, kmax=2, wmax=3, dtype="fp8")
+    cu = np.concatenate([[0], np.cumsum(LENS8)]).astype(np.int64)
+    d = to_device(inp)
+    got = pv.indexer_varlen(d["q"], d["w"], d["k"], cu, g=8, topk=32, C=96, mode=mode,
+                            q_scale=d["q_scale"], k_scale=d["k_scale"]).cpu().numpy()
+    assert got.shape == (cu[-1], 32)
+    for i, L in enumerate(LENS8):
+        if L == 0:
+            continue
+        a, b = int(cu[i]), int(cu[i + 1])
+        v = oracle.View("fp8", inp.q[a:b], inp.q_scale[a:b], inp.w[a:b], inp.k[a:b], inp.k_scale[a:b])
+        if mode == "dense":
+            ref = oracle.dense_rows(v, np.arange(L), 32)
+        else:
+            ref, _ = oracle.prefill_groups(v, L, 8, 32, 96, mode, np.arange((L + 7) // 8))
+        assert np.array_equal(got[a:b], ref), (mode, i)
