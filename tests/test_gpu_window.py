@@ -93,6 +93,19 @@ def test_window_chunked_passes_and_long_window(wmode):
             assert np.array_equal(got, ref), (mode, W)
 
 
+@pytest.mark.parametrize("wmode", ["shared", "excluded"])
+@pytest.mark.parametrize("mode", ["dense", "reuse", "refine"])
+def test_window_fp8_prefill_bit_exact(mode, wmode):
+    # fp8 codes of small integers with unit scales (every sum exact)
+    print(f"case: fp8 prefill L=900 H=8 D=64 g=8 k=48 C=120 {mode} window 37 {wmode}", flush=True)
+    inp = synth.small_integer(900, 8, 64, seed=63, qmax=2, kmax=2, wmax=3, dtype="fp8")
+    got = _run(inp, mode, 8, 48, 120, 37, wmode)
+    ref = _oracle(inp, mode, 8, 48, 120, 37, wmode)
+    assert got.shape == ref.shape == (900, 48 + 37)
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5]}"
+
+
 def test_window_zero_equals_plain(tiny):
     print("case: window 0 through the window entry point", flush=True)
     d = to_device(tiny)
