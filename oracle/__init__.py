@@ -18,8 +18,12 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PIVOT_ORACLE_LIB names a prebuilt variant of the same source (the planted-
+# mistake test builds such variants to show that the pins catch them)
+_VARIANT = os.environ.get("PIVOT_ORACLE_LIB")
+_LIB_PATH = _VARIANT or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "pivot_oracle.c")
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
 
 BF16, FP8 = 0, 1
 DENSE, REUSE, REFINE = 0, 1, 2
@@ -29,10 +33,10 @@ MODES = {"dense": DENSE, "reuse": REUSE, "refine": REFINE}
 def build(force: bool = False) -> str:
     """Compile pivot_oracle.c with gcc (plain -O2, IEEE binary32/binary64, no
     contraction of multiply-adds, single-threaded)."""
+    if _VARIANT:
+        return _LIB_PATH
     if force or not os.path.exists(_LIB_PATH):
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-o", _LIB_PATH, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
+        subprocess.run(["gcc", *CFLAGS, "-o", _LIB_PATH, _SRC, "-lm"], check=True)
     return _LIB_PATH
 
 
