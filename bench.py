@@ -68,7 +68,7 @@ def upload(inp, torch):
     def codes(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
+        return torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
 
     def f32(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
@@ -81,14 +81,31 @@ def upload(inp, torch):
 
 
 def time_steps(fn, steps, warmup, torch):
+    """Median seconds per call over `steps` calls (after `warmup`), each call
+    bracketed by two events on the current stream, the one the library
+    launches on."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
         fn()
+        b.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def measure_decode(torch, pv, synth, nd_steps, nd_prof):
@@ -109,14 +126,7 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
                           mode=mode, q_scale=dd["q_scale"], k_scale=dd["k_scale"], out=dout,
                           workspace=dws)
 
-    for _ in range(10):
-        dstep()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(nd_steps):
-        dstep()
-    torch.cuda.synchronize()
-    dsec = (time.perf_counter() - t0) / nd_steps
+    dsec = time_steps(dstep, nd_steps, 10, torch)
     pv.profile_enable(True)
     pv.profile_read()
     for _ in range(nd_prof):
@@ -126,11 +136,11 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
     pv.profile_enable(False)
     key_bytes = float(dec.cache_len.astype(np.int64).sum()) * (D + 4)
     scan_ms_d = dprof["decode_scan"][0] / nd_prof
-    dense_dsec = time_steps(lambda: dstep("dense"), max(1, nd_steps // 2), 5, torch)
+    dense_dsec = time_steps(lambda: dstep("dense"), nd_steps, 5, torch)
     # the same step over a paged cache: 64-key pages of a shuffled pool
     log("laying the decode cache out in 64-key pages")
     pc = synth.paged_cache(dec, 64)
-    kp = torch.from_numpy(pc.k_pages).cuda()
+    kp = torch.from_numpy(pc.k_pages).view(torch.float8_e4m3fn).cuda()
     ksp = torch.from_numpy(pc.k_scale_pages).cuda()
     btd = torch.from_numpy(pc.block_table).cuda()
 
@@ -162,7 +172,7 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
                                                   topk=topk, C=C, mode="refine",
                                                   q_scale=dd4["q_scale"], k_scale=dd4["k_scale"],
                                                   out=out4, workspace=ws4),
-                        max(1, nd_steps // 2), 5, torch)
+                        nd_steps, 5, torch)
     del dd4, ws4, out4
     res = {
         "workload": "decode_mtp_b32 (B=32, g=2, fp8, cache 32K-128K)",
@@ -186,7 +196,7 @@ def measure_decode(torch, pv, synth, nd_steps, nd_prof):
     return res
 
 
-def measure_prefill(torch, pv, d, L, modes, peak, g=8, topk=2048, C=4096, steps=5):
+def measure_prefill(torch, pv, d, L, modes, peak, g=8, topk=2048, C=4096, steps=10):
     """ms per call and queries/s of one prefill workload (g=8 groups; dense is
     g=1), and the full-prefix scan's matrix-core rate from the library's
     per-launch events against `peak` (the code type's dense peak)."""
@@ -200,7 +210,7 @@ def measure_prefill(torch, pv, d, L, modes, peak, g=8, topk=2048, C=4096, steps=
                          dtype=torch.uint8, device="cuda")
         f = lambda: pv.indexer(d["q"], d["w"], d["k"], g=gg, topk=topk, C=cc, mode=mode, out=out,
                                workspace=ws, q_scale=d.get("q_scale"), k_scale=d.get("k_scale"))
-        s = time_steps(f, steps, 1, torch)
+        s = time_steps(f, steps, 3, torch)
         pv.profile_enable(True)
         pv.profile_read()
         f()
@@ -246,7 +256,7 @@ def measure_attention(torch, pv, synth):
     ws = torch.empty(max(256, pv.load().pivot_sparse_attention_workspace_size(B * g, Hq, d, 2048)),
                      dtype=torch.uint8, device="cuda")
     f = lambda: pv.sparse_attention(qa, kc, vc, idx, rows_per_seq=g, out=out, workspace=ws)
-    sec = time_steps(f, 50, 5, torch)
+    sec = time_steps(f, 200, 10, torch)
     nsel = float((idx >= 0).sum().item())
     gb = nsel * 2 * d * 2 + qa.numel() * 2 + out.numel() * 4
     res["decode_b32"] = {"us_per_step": sec * 1e6, "selected_positions": nsel,
@@ -264,7 +274,7 @@ def measure_attention(torch, pv, synth):
     qp = torch.randn((L, Hq, d), generator=gen, device="cuda").to(torch.bfloat16)
     out = torch.empty((L, Hq, d), dtype=torch.float32, device="cuda")
     f = lambda: pv.sparse_attention(qp, kp, vp, rows, out=out)
-    sec = time_steps(f, 3, 1, torch)
+    sec = time_steps(f, 10, 3, torch)
     nsel = float((rows >= 0).sum().item())
     fl = 2.0 * Hq * 2 * d * nsel
     res["prefill_16k"] = {"ms_per_call": sec * 1e3, "selected_positions": nsel,
@@ -462,7 +472,7 @@ def main():
         log("timing the dense indexer")
         sec_d = time_steps(lambda: pv.indexer(d["q"], d["w"], d["k"], g=1, topk=topk, C=topk,
                                               mode="dense", out=out_d, workspace=ws_d),
-                           2, 1, torch)
+                           10, 2, torch)
         extras["dense_ms_per_step"] = sec_d * 1e3
         extras["dense_queries_per_s"] = L / sec_d
         extras["refine_speedup_vs_dense"] = sec_d / sec
@@ -493,11 +503,11 @@ def main():
                                dtype=torch.uint8, device="cuda")
             s = time_steps(lambda: pv.indexer(d["q"], d["w"], d["k"], g=gg, topk=topk,
                                               C=2 * topk, mode="refine", out=out, workspace=ws_g),
-                           3, 1, torch)
+                           10, 3, torch)
             sweep[f"refine_g{gg}"] = {"ms_per_step": s * 1e3, "queries_per_s": L / s,
                                       "speedup_vs_dense": sec_d / s}
         s = time_steps(lambda: pv.indexer(d["q"], d["w"], d["k"], g=8, topk=topk, C=C,
-                                          mode="reuse", out=out, workspace=ws), 3, 1, torch)
+                                          mode="reuse", out=out, workspace=ws), 10, 3, torch)
         sweep["reuse_g8"] = {"ms_per_step": s * 1e3, "queries_per_s": L / s,
                              "speedup_vs_dense": sec_d / s}
         extras["g_sweep"] = sweep
@@ -508,7 +518,7 @@ def main():
         for wm in ("shared", "excluded"):
             f = lambda: pv.indexer(d["q"], d["w"], d["k"], g=g, topk=topk, C=C, mode="refine",
                                    out=out_w, workspace=ws, window=W, window_mode=wm)
-            s = time_steps(f, 3, 1, torch)
+            s = time_steps(f, 10, 3, torch)
             pv.profile_enable(True)
             pv.profile_read()
             f()
@@ -535,7 +545,7 @@ def main():
         cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
         out_v = torch.empty((16384, topk), dtype=torch.int32, device="cuda")
         s_v = time_steps(lambda: pv.indexer_varlen(dv_["q"], dv_["w"], dv_["k"], cu, g=8, topk=topk, C=C,
-                                                   mode="refine", out=out_v), 5, 2, torch)
+                                                   mode="refine", out=out_v), 10, 3, torch)
         extras["varlen_refine_g8"] = {"lengths": lens, "ms_per_call": s_v * 1e3,
                                       "queries_per_s": 16384 / s_v}
         del out_v
@@ -565,7 +575,7 @@ def main():
             "value": cqps, "unit": "queries/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(groups)} whole Refine groups (g={g}, {len(groups)*g} queries) of "
                       f"the 128K workload, seeded-random group order, {cdt:.1f} s single-threaded",
-            "host": platform.processor() or platform.machine(),
+            "host": cpu_model(),
             "host_threads_available": os.cpu_count(),
         }
 

@@ -33,8 +33,8 @@
  *    must be ordered on one stream.
  *  - Arguments are validated on the host before anything is enqueued; on a
  *    non-zero status nothing was launched and `out` is untouched.  A failed
- *    launch returns PIVOT_ERR_HIP.  pivot_last_error() gives a message for the
- *    last failure on the calling thread.
+ *    launch returns PIVOT_ERR_HIP.  pivot_last_error_detail() gives a message
+ *    for the last failure on the calling thread.
  *  - Codes: bf16 (uint16 storage) or OCP FP8 E4M3FN (uint8 storage, finite
  *    max 448) with one float32 scale per token, which must be > 0.  NaN or Inf
  *    inputs are outside the contract.
@@ -59,11 +59,13 @@ extern "C" {
 typedef enum {
   PIVOT_OK = 0,
   PIVOT_ERR_NULL = 1,        /* a required pointer is NULL */
-  PIVOT_ERR_SHAPE = 2,       /* L, B, H, D, Lmax out of range or unsupported */
-  PIVOT_ERR_PARAM = 3,       /* g, topk, C, mode or dtype invalid (e.g. C < topk for Refine) */
-  PIVOT_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
-  PIVOT_ERR_WORKSPACE = 5,   /* workspace smaller than the minimum */
-  PIVOT_ERR_HIP = 6          /* a kernel launch failed */
+  PIVOT_ERR_SHAPE = 2,       /* L, B, H, Lmax, R ... out of range (e.g. L < 1, arrays too large) */
+  PIVOT_ERR_PARAM = 3,       /* g, topk, C, mode, dtype, window ... invalid (e.g. C < topk for Refine) */
+  PIVOT_ERR_UNSUPPORTED = 4, /* a valid shape the kernels are not built for (H > 64, D not in the set) */
+  PIVOT_ERR_ALIGN = 5,       /* a pointer is not aligned as required */
+  PIVOT_ERR_WORKSPACE = 6,   /* workspace smaller than the minimum */
+  PIVOT_ERR_HIP = 7,         /* a kernel launch failed */
+  PIVOT_ERR_INTERNAL = 8     /* an internal inconsistency (a bug in the library) */
 } pivot_status_t;
 
 typedef enum {
@@ -81,7 +83,8 @@ typedef enum {
 
 int pivot_version(void);
 const char* pivot_status_string(int status);
-const char* pivot_last_error(void);
+/* Message for the last failure on the calling thread (thread-local; "" if none). */
+const char* pivot_last_error_detail(void);
 
 /* ---------------------------------------------------------------------------
  * Prefill: one sequence of L queries over its own L keys (query t sits at
@@ -93,6 +96,11 @@ const char* pivot_last_error(void);
  *   w       [L][H] float head weights
  *   k       [L][D] codes              k_scale [L] float (fp8 only, else NULL)
  *   out     [L][topk] int32 positions
+ *   out_scores  optional [L][topk] float (NULL: not written): the binary32
+ *           score of each selected position as the kernels computed it (fp8:
+ *           with s_q * s_k applied) -- the member's own score for DENSE and
+ *           REFINE, the proxy's score for REUSE (the score that selected it);
+ *           NaN where out holds -1.  For tolerance checks against a reference.
  *   C       candidate-set size for Refine (C >= topk); ignored otherwise
  * Returns a pivot_status_t.
  * ------------------------------------------------------------------------- */
@@ -100,7 +108,8 @@ size_t pivot_workspace_size(int L, int H, int D, int g, int topk, int C, int mod
 size_t pivot_workspace_min_size(int L, int H, int D, int g, int topk, int C, int mode, int dtype);
 int pivot_indexer(const void* q, const float* q_scale, const float* w, const void* k,
                   const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
-                  int dtype, int32_t* out, void* workspace, size_t workspace_bytes, void* stream);
+                  int dtype, int32_t* out, float* out_scores, void* workspace, size_t workspace_bytes,
+                  void* stream);
 
 /* ---------------------------------------------------------------------------
  * Decode: one multi-token-prediction step for B sequences.  Sequence b holds
@@ -114,14 +123,15 @@ int pivot_indexer(const void* q, const float* q_scale, const float* w, const voi
  *   cache_len [B] int32, DEVICE memory; precondition g <= cache_len[b] <= Lmax
  *             (a sequence breaking it receives rows of -1)
  *   out       [B][g][topk] int32 positions
+ *   out_scores optional [B][g][topk] float, as for pivot_indexer (NULL: not written)
  * ------------------------------------------------------------------------- */
 size_t pivot_decode_workspace_size(int B, int Lmax, int H, int D, int g, int topk, int C,
                                    int mode, int dtype);
 int pivot_indexer_decode(const void* q, const float* q_scale, const float* w,
                          const void* k_cache, const float* k_scale, const int32_t* cache_len,
                          int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
-                         int dtype, int32_t* out, void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         int dtype, int32_t* out, float* out_scores, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Prefill and decode with a sliding window added to every query's selection
@@ -253,6 +263,17 @@ int pivot_sparse_attention(const void* q, const void* k, const void* v, const in
  *
  * pivot_decode_candidates: the same three steps for a decode step (one group
  * per sequence, the scan covering its whole cache): cand [B][m].
+ *
+ * pivot_dbg_score_rows: the indexer score rows themselves (tutorial "Sparse
+ * Attention의 Indexer", Figure 1: each query scores every key of its causal
+ * prefix), as the full-prefix scan kernel computes them.  Query row r of
+ * q [R][H][D] (with w [R][H], q_scale [R] for fp8) sees keys 0..p(r),
+ * p(r) = min(r * pos_mul + pos_add, Lk - 1), of k [Lk][D] (k_scale [Lk]):
+ *     S[(r - row_begin) * ldS + s] = sum_h w[r][h] * max(0, q[r][h] . k[s])
+ * (times q_scale[r] * k_scale[s] for fp8) for row_begin <= r < row_end and
+ * s <= p(r); every other entry of S is left untouched.  Dense rows are
+ * pos_mul = 1, pos_add = 0; the proxies of pivot_proxy_mean are rows of
+ * qbar with pos_mul = g, pos_add = g - 1.  ldS >= p(row_end - 1) + 1.
  * ------------------------------------------------------------------------- */
 int pivot_proxy_mean(const void* q, const float* q_scale, const float* w, int L, int H, int D,
                      int g, int dtype, void* qbar, float* qbar_scale, float* wbar, void* stream);
@@ -265,6 +286,9 @@ int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,
                             int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
                             int dtype, int32_t* cand, void* workspace, size_t workspace_bytes,
                             void* stream);
+int pivot_dbg_score_rows(const void* q, const float* q_scale, const float* w, const void* k,
+                         const float* k_scale, int R, int Lk, int H, int D, int dtype, int row_begin,
+                         int row_end, int pos_mul, int pos_add, float* S, long long ldS, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Per-kernel timing for measurement tools.  While enabled (process-wide),

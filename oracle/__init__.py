@@ -83,6 +83,9 @@ def lib():
             C.c_long, C.c_int, C.c_double, f64p]
         L.orc_score_row.argtypes = [C.POINTER(_View), C.c_int, C.c_int, f64p]
         L.orc_score_pairs.argtypes = [C.POINTER(_View), i32p, i32p, C.c_int, f64p]
+        L.orc_score_list.argtypes = [C.POINTER(_View), C.c_int, i32p, C.c_int, f64p]
+        L.orc_init.argtypes = []
+        L.orc_init()  # tables filled once, before any thread uses the oracle
         _lib = L
     return _lib
 
@@ -245,6 +248,15 @@ def group_rows(L: int, g: int, groups):
 def score_row(view: View, row: int, n: int):
     out = np.empty(n, np.float64)
     lib().orc_score_row(C.byref(view.c), row, n, out)
+    return out
+
+
+def score_list(view: View, row: int, keys):
+    """Scores of query row `row` against the listed keys."""
+    keys = np.ascontiguousarray(keys, np.int32)
+    out = np.empty(keys.shape[0], np.float64)
+    if keys.shape[0]:
+        lib().orc_score_list(C.byref(view.c), int(row), keys, keys.shape[0], out)
     return out
 
 

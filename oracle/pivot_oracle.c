@@ -487,3 +487,17 @@ void orc_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* 
   }
   free(sc);
 }
+
+/* Fills the E4M3 value table up front, so that later calls only read it
+ * (calls from several host threads then share no writes). */
+void orc_init(void) {
+  for (int c = 0; c < 256; ++c) e4m3_table[c] = orc_e4m3_value((uint8_t)c);
+  e4m3_table_ready = 1;
+}
+
+/* Scores of the query row `row` of the view against the listed keys (the same
+ * score as orc_score_row, for an arbitrary key list). */
+void orc_score_list(const orc_view* v, int row, const int32_t* keys, int n, double* out) {
+  const void* qc = code_ptr(v->dtype, v->q, (long)row * v->H * v->D);
+  score_keys(v, qc, row_scale(v, row), v->w + (long)row * v->H, keys, n, out);
+}

@@ -51,6 +51,10 @@ typedef struct {
   const float* k_scale;
 } orc_view;
 
+/* Fills the oracle's constant tables; call once before using the oracle from
+ * several host threads (each call is single-threaded and shares only these). */
+void orc_init(void);
+
 /* number formats */
 double orc_bf16_value(uint16_t code);
 double orc_e4m3_value(uint8_t code);
@@ -120,6 +124,9 @@ void orc_sparse_attention(const uint16_t* q, const uint16_t* k, const uint16_t* 
 
 /* Scores of the query row `row` of the view against keys [0, n). */
 void orc_score_row(const orc_view* v, int row, int n, double* out);
+
+/* Scores of the query row `row` against the n listed keys. */
+void orc_score_list(const orc_view* v, int row, const int32_t* keys, int n, double* out);
 
 /* Scores of arbitrary (query row, key) pairs. */
 void orc_score_pairs(const orc_view* v, const int32_t* rows, const int32_t* keys, int npairs,

@@ -8,9 +8,14 @@ accepts exactly those swaps: with tau the m-th largest oracle score of the
 pool, every position the GPU picked that the oracle did not must score at
 least tau - eps*|tau|, and every position the oracle picked that the GPU did
 not must score at most tau + eps*|tau|; the number of selected positions must
-match exactly.
+match exactly.  Scores the GPU reports for its selected positions must agree
+with the oracle's score of the same position: |s_gpu - s_orc| <=
+eps * max(|s_orc|, |tau|); entries past the selection are NaN.
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -23,13 +28,40 @@ EPS_BF16 = 1e-4
 # fp8 inputs: the stated score tolerance.
 EPS_FP8 = 2e-2
 
+# host threads for the oracle (its C calls release the interpreter lock); at
+# most 16, the host share of one GPU
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def pmap(fn, items):
+    """fn over items on THREADS host threads, results in order."""
+    items = list(items)
+    if THREADS == 1 or len(items) < 2:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(THREADS) as ex:
+        return list(ex.map(fn, items))
+
+
+def stratified_groups(G: int, n_extra: int, seed: int):
+    """The first two and last two groups plus one seeded group from each of
+    n_extra equal strata of the rest, so every part of the sequence (every
+    workspace pass and scan launch) is sampled."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, G - 2, G - 1]
+    if G <= 4 + n_extra:
+        return list(range(G))
+    edges = np.linspace(2, G - 2, n_extra + 1).astype(np.int64)
+    extra = [int(rng.integers(lo, hi)) for lo, hi in zip(edges[:-1], edges[1:]) if hi > lo]
+    return sorted(set(fixed + extra))
+
 
 def to_device(inp, device="cuda"):
-    """Upload PrefillInputs / DecodeInputs codes as raw device tensors."""
+    """Upload PrefillInputs / DecodeInputs codes as device tensors (bf16 or fp8)."""
     def codes(a):
+        a = np.ascontiguousarray(a)
         if a.dtype == np.uint16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a).view(torch.float8_e4m3fn).to(device)
 
     def f32(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
@@ -51,26 +83,55 @@ def check_row_shape(row, n_valid_expected, t=None):
         assert np.all(valid <= t), "a future position was selected"
 
 
-def check_band(gpu_row, pool_pos, pool_scores, m, eps, what=""):
+def check_scores(gpu_row, gpu_scores, pos_score, eps, tau, what=""):
+    """GPU scores of the selected positions against the oracle's scores of the
+    same positions (pos_score: array aligned with the valid entries)."""
+    gpu_row = np.asarray(gpu_row)
+    gs = np.asarray(gpu_scores, np.float64)
+    nv = int((gpu_row >= 0).sum())
+    assert np.all(np.isnan(gs[nv:])), f"{what}: scores past the selection must be NaN"
+    if nv == 0:
+        return
+    got = gs[:nv]
+    ref = np.asarray(pos_score, np.float64)
+    tol = eps * np.maximum(np.abs(ref), abs(tau))
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (f"{what}: score of position {gpu_row[:nv][bad][0]}: GPU {got[bad][0]!r}, "
+                           f"oracle {ref[bad][0]!r}")
+
+
+def check_band(gpu_row, pool_pos, pool_scores, m, eps, what="", gpu_scores=None):
     """gpu_row: selected positions (ascending, -1 padded) out of pool_pos whose
-    oracle scores are pool_scores."""
+    oracle scores are pool_scores; gpu_scores (optional): the GPU's scores of
+    its selected positions.  Returns the number of tie-band swaps."""
     pool_pos = np.asarray(pool_pos, np.int64)
     pool_scores = np.asarray(pool_scores, np.float64)
     n = len(pool_pos)
     r = min(m, n)
     gpu_row = np.asarray(gpu_row)
     check_row_shape(gpu_row, r)
-    g = set(gpu_row[gpu_row >= 0].tolist())
-    ref = oracle.topk(pool_scores, m, pool_pos.astype(np.int32))
-    o = set(ref[ref >= 0].tolist())
-    assert g <= set(pool_pos.tolist()), f"{what}: position outside the pool"
-    if g == o:
+    g = gpu_row[gpu_row >= 0].astype(np.int64)
+    order = np.argsort(pool_pos, kind="stable")
+    sp = pool_pos[order]
+    ss = pool_scores[order]
+    at = np.searchsorted(sp, g)
+    inpool = (at < n) & (sp[np.minimum(at, max(n - 1, 0))] == g) if n else np.zeros(len(g), bool)
+    assert inpool.all(), f"{what}: position {g[~inpool][0]} outside the pool"
+    gsc = ss[at] if n else np.zeros(0)
+    tau = float(np.partition(pool_scores, n - r)[n - r]) if r > 0 else 0.0
+    if gpu_scores is not None:
+        check_scores(gpu_row, gpu_scores, gsc, eps, tau, what)
+    if r == 0:
         return 0
-    score = dict(zip(pool_pos.tolist(), pool_scores.tolist()))
-    tau = np.sort(pool_scores)[::-1][r - 1]
+    ref = oracle.topk(pool_scores, m, pool_pos.astype(np.int32))
+    o = ref[ref >= 0].astype(np.int64)
+    if np.array_equal(g, o):
+        return 0
     band = eps * max(abs(tau), 1e-30)
-    for x in g - o:
-        assert score[x] >= tau - band, f"{what}: GPU picked {x} ({score[x]}) below tau {tau}"
-    for x in o - g:
-        assert score[x] <= tau + band, f"{what}: GPU dropped {x} ({score[x]}) above tau {tau}"
-    return len(g - o)
+    extra = np.setdiff1d(g, o)
+    missing = np.setdiff1d(o, g)
+    esc = ss[np.searchsorted(sp, extra)]
+    msc = ss[np.searchsorted(sp, missing)]
+    assert np.all(esc >= tau - band), f"{what}: GPU picked {extra[esc < tau - band][0]} below tau {tau}"
+    assert np.all(msc <= tau + band), f"{what}: GPU dropped {missing[msc > tau + band][0]} above tau {tau}"
+    return len(extra)

@@ -12,7 +12,9 @@ from conftest import ROOT
 
 HEADER = os.path.join(ROOT, "include", "pivot.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_ALIGN, ERR_WORKSPACE = 0, 1, 2, 3, 4, 5
+# the status set of include/pivot.h
+(OK, ERR_NULL, ERR_SHAPE, ERR_PARAM, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_HIP,
+ ERR_INTERNAL) = range(9)
 FAKE = 0x100000  # aligned, never dereferenced
 
 
@@ -36,15 +38,27 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert lib.pivot_version() >= 100
+    for n in ("pivot_last_error_detail", "pivot_dbg_score_rows", "pivot_indexer", "pivot_indexer_decode"):
+        assert n in names, n
+
+
+def test_status_strings(lib):
+    seen = set()
+    for st in range(9):
+        msg = lib.pivot_status_string(st).decode()
+        assert msg and msg != "unknown status", st
+        seen.add(msg)
+    assert len(seen) == 9
+    assert lib.pivot_status_string(99).decode() == "unknown status"
 
 
 def _call(lib, **kw):
     a = dict(q=FAKE, qs=None, w=FAKE, k=FAKE, ks=None, L=2048, H=4, D=32, g=4, topk=64, C=256,
-             mode=pv.REFINE, dtype=0, out=FAKE, ws=FAKE, wsb=1 << 40, st=None)
+             mode=pv.REFINE, dtype=0, out=FAKE, scores=None, ws=FAKE, wsb=1 << 40, st=None)
     a.update(kw)
     return lib.pivot_indexer(a["q"], a["qs"], a["w"], a["k"], a["ks"], a["L"], a["H"], a["D"],
-                             a["g"], a["topk"], a["C"], a["mode"], a["dtype"], a["out"], a["ws"],
-                             a["wsb"], a["st"])
+                             a["g"], a["topk"], a["C"], a["mode"], a["dtype"], a["out"], a["scores"],
+                             a["ws"], a["wsb"], a["st"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -54,9 +68,9 @@ def _call(lib, **kw):
     (dict(ws=None), ERR_NULL),
     (dict(dtype=1), ERR_NULL),               # fp8 without scales
     (dict(H=0), ERR_SHAPE),
-    (dict(H=65), ERR_SHAPE),
-    (dict(D=48), ERR_SHAPE),
-    (dict(D=32, dtype=1, qs=FAKE, ks=FAKE), ERR_SHAPE),  # fp8 needs D in {64,128,256}
+    (dict(H=65), ERR_UNSUPPORTED),
+    (dict(D=48), ERR_UNSUPPORTED),
+    (dict(D=32, dtype=1, qs=FAKE, ks=FAKE), ERR_UNSUPPORTED),  # fp8 needs D in {64,128,256}
     (dict(L=0), ERR_SHAPE),
     (dict(g=0), ERR_PARAM),
     (dict(topk=0), ERR_PARAM),
@@ -67,11 +81,13 @@ def _call(lib, **kw):
     (dict(k=FAKE + 4), ERR_ALIGN),
     (dict(w=FAKE + 2), ERR_ALIGN),
     (dict(ws=FAKE + 64), ERR_ALIGN),
+    (dict(scores=FAKE + 2), ERR_ALIGN),
     (dict(wsb=1024), ERR_WORKSPACE),
+    (dict(scores=FAKE, wsb=1024), ERR_WORKSPACE),  # scores are optional output only
 ])
 def test_prefill_validation(lib, kw, status):
     assert _call(lib, **kw) == status
-    assert lib.pivot_last_error()  # a message is recorded
+    assert lib.pivot_last_error_detail()  # a message is recorded
 
 
 def test_reuse_ignores_C(lib):
@@ -82,11 +98,11 @@ def test_reuse_ignores_C(lib):
 def test_decode_validation(lib):
     f = lib.pivot_indexer_decode
     base = [FAKE, None, FAKE, FAKE, None, FAKE, 32, 131072, 64, 128, 2, 2048, 4096, pv.REFINE, 0,
-            FAKE, FAKE, 1 << 40, None]
+            FAKE, None, FAKE, 1 << 40, None]
     def call(**kw):
         a = list(base)
         idx = dict(q=0, w=2, k=3, cl=5, B=6, Lmax=7, H=8, D=9, g=10, topk=11, C=12, mode=13,
-                   dtype=14, out=15, ws=16, wsb=17)
+                   dtype=14, out=15, scores=16, ws=17, wsb=18)
         for k_, v in kw.items():
             a[idx[k_]] = v
         return f(*a)
@@ -96,6 +112,32 @@ def test_decode_validation(lib):
     assert call(C=100) == ERR_PARAM
     assert call(wsb=100) == ERR_WORKSPACE
     assert call(dtype=1) == ERR_NULL
+    assert call(H=65) == ERR_UNSUPPORTED
+    assert call(scores=FAKE + 1) == ERR_ALIGN
+    assert call(scores=FAKE, wsb=100) == ERR_WORKSPACE
+
+
+def test_score_rows_validation(lib):
+    def f(**kw):
+        a = dict(q=FAKE, qs=None, w=FAKE, k=FAKE, ks=None, R=64, Lk=4096, H=64, D=128, dt=0, rb=0, re=64,
+                 pm=1, pa=0, S=FAKE, ld=4096)
+        a.update(kw)
+        return lib.pivot_dbg_score_rows(a["q"], a["qs"], a["w"], a["k"], a["ks"], a["R"], a["Lk"], a["H"],
+                                        a["D"], a["dt"], a["rb"], a["re"], a["pm"], a["pa"], a["S"], a["ld"],
+                                        None)
+    assert f(q=None) == ERR_NULL
+    assert f(S=None) == ERR_NULL
+    assert f(dt=1) == ERR_NULL  # fp8 needs scales
+    assert f(R=0) == ERR_SHAPE
+    assert f(re=65) == ERR_SHAPE
+    assert f(rb=10, re=5) == ERR_SHAPE
+    assert f(H=65) == ERR_UNSUPPORTED
+    assert f(D=96) == ERR_UNSUPPORTED
+    assert f(pm=-1) == ERR_PARAM
+    assert f(ld=63) == ERR_PARAM  # the last row sees keys 0..63
+    assert f(S=FAKE + 2) == ERR_ALIGN
+    assert f(rb=5, re=5) == OK    # no rows: nothing to launch
+
 
 
 def test_workspace_sizes(lib):
@@ -151,8 +193,8 @@ def test_sparse_attention_validation(lib):
                                           a["dv"], a["nidx"], a["rps"], a["stride"], a["seq_len"],
                                           a["scale"], a["out"], a["ws"], a["wsb"], None)
     assert f(q=None) == ERR_NULL
-    assert f(Hq=48) == ERR_SHAPE
-    assert f(d=64) == ERR_SHAPE
+    assert f(Hq=48) == ERR_UNSUPPORTED
+    assert f(d=64) == ERR_UNSUPPORTED
     assert f(R=0) == ERR_SHAPE
     assert f(rps=0) == ERR_PARAM
     assert f(stride=100) == ERR_PARAM          # sequences would overlap

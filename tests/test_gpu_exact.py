@@ -130,6 +130,73 @@ def test_tiny_proxy_bits_and_candidates(tiny):
         assert np.array_equal(cand, ref)
 
 
+@pytest.mark.parametrize("mode", ["dense", "reuse", "refine"])
+def test_tiny_scores_exact(tiny, mode):
+    """The scores returned with the selection are the exact scores on the tiny
+    workload (every binary32 sum is exact there): the member's own score for
+    dense and Refine, the proxy's score for Reuse; NaN past the selection."""
+    print(f"case: tiny prefill scores, {mode}", flush=True)
+    d = to_device(tiny)
+    out, sc = pv.indexer(d["q"], d["w"], d["k"], g=4, topk=64, C=256, mode=mode, return_scores=True)
+    torch.cuda.synchronize()
+    out, sc = out.cpu().numpy(), sc.cpu().numpy()
+    assert np.array_equal(out, _oracle_all(tiny, mode, 4, 64, 256))
+    v = oracle.View.of(tiny)
+    for j in range(2048 // 4):
+        psc = oracle.group(v, 4 * j, 4 * j, 4, 64, 256, "reuse")[2] if mode == "reuse" else None
+        for t in range(4 * j, 4 * j + 4):
+            sel = out[t][out[t] >= 0]
+            ref = psc[sel] if mode == "reuse" else oracle.score_list(v, t, sel)
+            assert np.array_equal(sc[t][:len(sel)].astype(np.float64), ref), t
+            assert np.all(np.isnan(sc[t][len(sel):])), t
+
+
+def test_tiny_score_rows_exact(tiny):
+    """The score-row export: dense rows and proxy rows of the tiny workload
+    equal the oracle's exact scores on every key of their prefix."""
+    print("case: tiny prefill score rows (dense and proxy rows)", flush=True)
+    d = to_device(tiny)
+    v = oracle.View.of(tiny)
+    S = pv.score_rows(d["q"], d["w"], d["k"]).cpu().numpy()
+    for t in (0, 1, 63, 64, 1000, 2047):
+        assert np.array_equal(S[t][:t + 1].astype(np.float64), oracle.score_row(v, t, t + 1)), t
+        assert np.all(np.isnan(S[t][t + 1:])), t
+    qbar, _, wbar = pv.proxy_mean(d["q"], d["w"], 4)
+    P = pv.score_rows(qbar, wbar, d["k"], pos_mul=4, pos_add=3).cpu().numpy()
+    for j in (0, 1, 100, 511):
+        pq, _, pw = oracle.proxy(v, 4 * j, 4)
+        e = 4 * j + 3
+        ref = oracle.score_row(oracle.View("bf16", pq[None], None, pw[None], tiny.k, None), 0, e + 1)
+        assert np.array_equal(P[j][:e + 1].astype(np.float64), ref), j
+        assert np.all(np.isnan(P[j][e + 1:])), j
+    # a window of rows: only rows [row_begin, row_end) are written
+    part = pv.score_rows(d["q"], d["w"], d["k"], row_begin=500, row_end=520).cpu().numpy()
+    assert np.array_equal(np.nan_to_num(part, nan=-1.0), np.nan_to_num(S[500:520], nan=-1.0))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_decode_scores_exact(dtype):
+    """Decode on integer-valued inputs (bf16, and fp8 with unit scales): the
+    scores of every mode are exact."""
+    print(f"case: decode scores on integer inputs, B=5, {dtype}", flush=True)
+    lens = [2, 37, 1000, 999, 1500]
+    dec = _decode_inputs(5, lens, g=2, H=8, D=64, Lmax=1500, dtype=dtype)
+    d = to_device(dec)
+    for mode in ("dense", "reuse", "refine"):
+        out, sc = pv.indexer_decode(d["q"], d["w"], d["k"], d["cache_len"], topk=40, C=100, mode=mode,
+                                    q_scale=d["q_scale"], k_scale=d["k_scale"], return_scores=True)
+        out, sc = out.cpu().numpy(), sc.cpu().numpy()
+        for b in range(dec.B):
+            v = oracle.decode_view(dec, b)
+            ref_rows, _, psc = oracle.decode_seq(dec, b, 40, 100, mode)
+            assert np.array_equal(out[b], ref_rows), (mode, b)
+            for i in range(2):
+                sel = out[b, i][out[b, i] >= 0]
+                ref = psc[sel] if mode == "reuse" else oracle.score_list(v, i, sel)
+                assert np.array_equal(sc[b, i][:len(sel)].astype(np.float64), ref), (mode, b, i)
+                assert np.all(np.isnan(sc[b, i][len(sel):]))
+
+
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
 def test_float_proxy_bits(dtype):
     # a short sequence (every group checked) and a longer one (sampled groups)

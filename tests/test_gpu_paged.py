@@ -37,7 +37,7 @@ def _pages_dev(pc):
     if pc.k_pages.dtype == np.uint16:
         kp = torch.from_numpy(pc.k_pages.view(np.int16)).view(torch.bfloat16).cuda()
     else:
-        kp = torch.from_numpy(pc.k_pages).cuda()
+        kp = torch.from_numpy(pc.k_pages).view(torch.float8_e4m3fn).cuda()
     ks = None if pc.k_scale_pages is None else torch.from_numpy(pc.k_scale_pages).cuda()
     return kp, ks, torch.from_numpy(pc.block_table).cuda()
 

@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "DENSE", "REUSE", "REFINE", "PivotError", "library_path", "load",
-    "indexer", "indexer_decode", "indexer_decode_paged", "indexer_varlen",
+    "indexer", "indexer_decode", "indexer_decode_paged", "indexer_varlen", "score_rows",
     "sparse_attention", "proxy_mean", "candidates", "decode_candidates",
     "workspace_size",
     "decode_workspace_size", "selftest_mfma_layout",
@@ -60,13 +60,13 @@ def load():
     L.pivot_version.restype = i
     L.pivot_status_string.restype = C.c_char_p
     L.pivot_status_string.argtypes = [i]
-    L.pivot_last_error.restype = C.c_char_p
+    L.pivot_last_error_detail.restype = C.c_char_p
     L.pivot_workspace_size.restype = sz
     L.pivot_workspace_size.argtypes = [i] * 8
     L.pivot_workspace_min_size.restype = sz
     L.pivot_workspace_min_size.argtypes = [i] * 8
     L.pivot_indexer.restype = i
-    L.pivot_indexer.argtypes = [vp, fp, fp, vp, fp] + [i] * 8 + [ip, vp, sz, vp]
+    L.pivot_indexer.argtypes = [vp, fp, fp, vp, fp] + [i] * 8 + [ip, fp, vp, sz, vp]
     L.pivot_candidates.restype = i
     L.pivot_candidates.argtypes = [vp, fp, fp, vp, fp] + [i] * 8 + [ip, vp, sz, vp]
     L.pivot_proxy_mean.restype = i
@@ -74,7 +74,9 @@ def load():
     L.pivot_decode_workspace_size.restype = sz
     L.pivot_decode_workspace_size.argtypes = [i] * 9
     L.pivot_indexer_decode.restype = i
-    L.pivot_indexer_decode.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, vp, sz, vp]
+    L.pivot_indexer_decode.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, fp, vp, sz, vp]
+    L.pivot_dbg_score_rows.restype = i
+    L.pivot_dbg_score_rows.argtypes = [vp, fp, fp, vp, fp] + [i] * 9 + [fp, C.c_longlong, vp]
     L.pivot_indexer_window.restype = i
     L.pivot_indexer_window.argtypes = [vp, fp, fp, vp, fp] + [i] * 10 + [ip, vp, sz, vp]
     L.pivot_indexer_decode_window.restype = i
@@ -106,7 +108,7 @@ def _check(status: int):
     if status != 0:
         L = load()
         raise PivotError(f"{L.pivot_status_string(status).decode()}: "
-                         f"{L.pivot_last_error().decode()}")
+                         f"{L.pivot_last_error_detail().decode()}")
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -120,15 +122,43 @@ def _stream(stream) -> int:
 
 
 def _mode(mode) -> int:
-    return _MODES[mode] if isinstance(mode, str) else int(mode)
+    m = _MODES.get(mode, -1) if isinstance(mode, str) else int(mode)
+    if m not in (DENSE, REUSE, REFINE):
+        raise PivotError(f"mode {mode!r} is not dense, reuse or refine")
+    return m
+
+
+_CODE_TYPES = {torch.bfloat16: BF16, torch.float8_e4m3fn: FP8}
 
 
 def _dtype_of(q: torch.Tensor) -> int:
-    if q.element_size() == 2:
-        return BF16
-    if q.element_size() == 1:
-        return FP8
-    raise PivotError(f"unsupported code type {q.dtype}: use bf16 (2-byte) or fp8 e4m3 (1-byte)")
+    dt = _CODE_TYPES.get(q.dtype)
+    if dt is None:
+        raise PivotError(f"unsupported code type {q.dtype}: use torch.bfloat16 or torch.float8_e4m3fn")
+    return dt
+
+
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype=None, optional=False):
+    """Shape and dtype checks that run before anything touches the device."""
+    if t is None:
+        if optional:
+            return None
+        raise PivotError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise PivotError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise PivotError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise PivotError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _scales(dt: int, q_scale, k_scale, qs_shape, ks_shape):
+    if dt == FP8:
+        _expect(q_scale, "q_scale", qs_shape, torch.float32)
+        _expect(k_scale, "k_scale", ks_shape, torch.float32)
+    elif q_scale is not None or k_scale is not None:
+        raise PivotError("bf16 inputs take no q_scale / k_scale")
 
 
 def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
@@ -143,6 +173,11 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
     return t
 
 
+def _on_device(**tensors):
+    for name, t in tensors.items():
+        _dev(t, name)
+
+
 def workspace_size(L, H, D, g, topk, C, mode, dtype) -> int:
     return load().pivot_workspace_size(L, H, D, g, topk, C, _mode(mode), dtype)
 
@@ -154,10 +189,12 @@ def decode_workspace_size(B, Lmax, H, D, g, topk, C, mode, dtype) -> int:
 def _workspace(nbytes: int, device, workspace, min_bytes: Optional[int] = None):
     """The caller's workspace (at least min_bytes, default nbytes) or a new one of nbytes."""
     if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise PivotError("workspace must be a 1-D torch.uint8 tensor")
+        _dev(workspace, "workspace")
         need = nbytes if min_bytes is None else min_bytes
-        if workspace.numel() * workspace.element_size() < need:
-            raise PivotError(f"workspace of {workspace.numel() * workspace.element_size()} bytes "
-                             f"is below the minimum {need}")
+        if workspace.numel() < need:
+            raise PivotError(f"workspace of {workspace.numel()} bytes is below the minimum {need}")
         return workspace
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
@@ -166,39 +203,71 @@ WINDOW_MODES = {"shared": 0, "excluded": 1}
 
 
 def _window_mode(wm) -> int:
-    return WINDOW_MODES[wm] if isinstance(wm, str) else int(wm)
+    m = WINDOW_MODES.get(wm, -1) if isinstance(wm, str) else int(wm)
+    if m not in (0, 1):
+        raise PivotError(f"window_mode {wm!r} is not shared or excluded")
+    return m
+
+
+def _prefill_inputs(q, w, k, q_scale, k_scale):
+    """Checks one sequence's q [L,H,D], w [L,H], k [L,D] (+ fp8 scales [L])."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise PivotError("q must be a [L, H, D] tensor")
+    dt = _dtype_of(q)
+    Lq, H, D = q.shape
+    _expect(w, "w", (Lq, H), torch.float32)
+    _expect(k, "k", (Lq, D), q.dtype)
+    _scales(dt, q_scale, k_scale, (Lq,), (Lq,))
+    return dt, Lq, H, D
+
+
+def _out(out, name, shape, dtype, device):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _expect(out, name, shape, dtype)
+    _dev(out, name)
+    return out
 
 
 def indexer(q, w, k, *, g: int, topk: int, C: int = 0, mode="refine", q_scale=None,
             k_scale=None, out=None, workspace=None, stream=None, window: int = 0,
-            window_mode="shared") -> torch.Tensor:
+            window_mode="shared", out_scores=None, return_scores: bool = False):
     """Prefill indexer for one sequence.
 
-    q [L,H,D] bf16 or fp8 codes, w [L,H] float32, k [L,D] codes; fp8 needs
-    q_scale [L] and k_scale [L] float32.  Returns int32 [L, topk]: ascending
-    selected positions, -1 padded.  window > 0 adds the sliding window of that
-    size to every row (window_mode "shared" or "excluded", as in
-    pivot_indexer_window) and returns [L, topk + window].
+    q [L,H,D] bf16 or fp8 (float8_e4m3fn) codes, w [L,H] float32, k [L,D]
+    codes of q's type; fp8 needs q_scale [L] and k_scale [L] float32.  Returns
+    int32 [L, topk]: ascending selected positions, -1 padded.  window > 0 adds
+    the sliding window of that size to every row (window_mode "shared" or
+    "excluded", as in pivot_indexer_window) and returns [L, topk + window].
+    With return_scores (or a float32 [L, topk] out_scores; no window) the
+    score of every selected position is written too and (out, scores) is
+    returned.
     """
     L = load()
-    q, w, k = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k, "k")
-    q_scale, k_scale = _dev(q_scale, "q_scale", torch.float32), _dev(k_scale, "k_scale", torch.float32)
-    Lq, H, D = q.shape
-    dt = _dtype_of(q)
+    dt, Lq, H, D = _prefill_inputs(q, w, k, q_scale, k_scale)
     m = _mode(mode)
-    if out is None:
-        out = torch.empty((Lq, topk + window), dtype=torch.int32, device=q.device)
+    if window < 0:
+        raise PivotError("window must be >= 0")
+    wm = _window_mode(window_mode)
+    out = _out(out, "out", (Lq, topk + window), torch.int32, q.device)
+    want = return_scores or out_scores is not None
+    if want:
+        if window:
+            raise PivotError("scores are returned without a window only")
+        out_scores = _out(out_scores, "out_scores", (Lq, topk), torch.float32, q.device)
+    _on_device(q=q, w=w, k=k, q_scale=q_scale, k_scale=k_scale)
     ws = _workspace(L.pivot_workspace_size(Lq, H, D, g, topk, C, m, dt), q.device, workspace,
                     L.pivot_workspace_min_size(Lq, H, D, g, topk, C, m, dt))
-    nbytes = ws.numel() * ws.element_size()
+    nbytes = ws.numel()
     if window:
         _check(L.pivot_indexer_window(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), Lq,
-                                      H, D, g, topk, C, m, dt, window, _window_mode(window_mode),
+                                      H, D, g, topk, C, m, dt, window, wm,
                                       _ptr(out), _ptr(ws), nbytes, _stream(stream)))
     else:
         _check(L.pivot_indexer(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), Lq, H, D,
-                               g, topk, C, m, dt, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
-    return out
+                               g, topk, C, m, dt, _ptr(out), _ptr(out_scores), _ptr(ws), nbytes,
+                               _stream(stream)))
+    return (out, out_scores) if want else out
 
 
 def indexer_varlen(q, w, k, cu_seqlens, *, g: int, topk: int, C: int = 0, mode="refine",
@@ -206,25 +275,25 @@ def indexer_varlen(q, w, k, cu_seqlens, *, g: int, topk: int, C: int = 0, mode="
                    workspace=None, stream=None) -> torch.Tensor:
     """Several prefill sequences in one call (pivot_indexer_varlen): q [T,H,D],
     w [T,H], k [T,D] hold the sequences back to back; cu_seqlens (host ints,
-    nseq + 1 offsets starting at 0) delimits them.  Returns int32
-    [T, topk + window]; each sequence's rows are those of indexer() on it alone."""
+    nseq + 1 offsets starting at 0 and ending at T) delimits them.  Returns
+    int32 [T, topk + window]; each sequence's rows are those of indexer() on it
+    alone."""
     import numpy as np
     L = load()
-    q, w, k = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k, "k")
-    q_scale, k_scale = _dev(q_scale, "q_scale", torch.float32), _dev(k_scale, "k_scale", torch.float32)
+    dt, T, H, D = _prefill_inputs(q, w, k, q_scale, k_scale)
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    if cu.ndim != 1 or cu.shape[0] < 2 or cu[0] != 0 or cu[-1] != T:
+        raise PivotError(f"cu_seqlens must be 1-D offsets from 0 to {T}")
     nseq = cu.shape[0] - 1
-    T, H, D = q.shape
-    dt = _dtype_of(q)
     m = _mode(mode)
-    if out is None:
-        out = torch.empty((T, topk + window), dtype=torch.int32, device=q.device)
+    wm = _window_mode(window_mode)
+    out = _out(out, "out", (T, topk + window), torch.int32, q.device)
+    _on_device(q=q, w=w, k=k, q_scale=q_scale, k_scale=k_scale)
     ws = _workspace(L.pivot_varlen_workspace_size(cu.ctypes.data, nseq, H, D, g, topk, C, m, dt),
                     q.device, workspace)
     _check(L.pivot_indexer_varlen(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale),
-                                  cu.ctypes.data, nseq, H, D, g, topk, C, m, dt, window,
-                                  _window_mode(window_mode), _ptr(out), _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream(stream)))
+                                  cu.ctypes.data, nseq, H, D, g, topk, C, m, dt, window, wm,
+                                  _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
@@ -232,26 +301,31 @@ def candidates(q, w, k, *, g: int, topk: int, C: int = 0, mode="refine", q_scale
                k_scale=None, workspace=None, stream=None) -> torch.Tensor:
     """Every group's proxy top-m (m = C for Refine, topk for Reuse): int32 [G, m]."""
     L = load()
-    q, w, k = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k, "k")
-    Lq, H, D = q.shape
-    dt = _dtype_of(q)
+    dt, Lq, H, D = _prefill_inputs(q, w, k, q_scale, k_scale)
     m = _mode(mode)
     G = (Lq + g - 1) // g
+    _on_device(q=q, w=w, k=k, q_scale=q_scale, k_scale=k_scale)
     cand = torch.empty((G, C if m == REFINE else topk), dtype=torch.int32, device=q.device)
     ws = _workspace(L.pivot_workspace_size(Lq, H, D, g, topk, C, m, dt), q.device, workspace,
                     L.pivot_workspace_min_size(Lq, H, D, g, topk, C, m, dt))
     _check(L.pivot_candidates(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), Lq, H, D,
-                              g, topk, C, m, dt, _ptr(cand), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(stream)))
+                              g, topk, C, m, dt, _ptr(cand), _ptr(ws), ws.numel(), _stream(stream)))
     return cand
 
 
 def proxy_mean(q, w, g: int, q_scale=None, stream=None):
     """Proxy codes [G,H,D] (same code type as q), proxy scales [G] and weights [G,H]."""
     L = load()
-    q, w = _dev(q, "q"), _dev(w, "w", torch.float32)
-    Lq, H, D = q.shape
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise PivotError("q must be a [L, H, D] tensor")
     dt = _dtype_of(q)
+    Lq, H, D = q.shape
+    _expect(w, "w", (Lq, H), torch.float32)
+    if dt == FP8:
+        _expect(q_scale, "q_scale", (Lq,), torch.float32)
+    elif q_scale is not None:
+        raise PivotError("bf16 inputs take no q_scale")
+    _on_device(q=q, w=w, q_scale=q_scale)
     G = (Lq + g - 1) // g
     qbar = torch.empty((G, H, D), dtype=q.dtype, device=q.device)
     qs = torch.empty(G, dtype=torch.float32, device=q.device)
@@ -261,34 +335,83 @@ def proxy_mean(q, w, g: int, q_scale=None, stream=None):
     return qbar, qs, wbar
 
 
+def score_rows(q, w, k, *, row_begin: int = 0, row_end: Optional[int] = None, pos_mul: int = 1,
+               pos_add: int = 0, q_scale=None, k_scale=None, stream=None) -> torch.Tensor:
+    """Indexer score rows as the full-prefix scan computes them
+    (pivot_dbg_score_rows): q [R,H,D] query rows (raw queries, or the proxies
+    of proxy_mean with pos_mul = g, pos_add = g - 1), w [R,H], k [Lk,D]; row r
+    sees keys 0..min(r*pos_mul + pos_add, Lk-1).  Returns float32
+    [row_end - row_begin, Lk]; entries past a row's last key are NaN."""
+    L = load()
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise PivotError("q must be a [R, H, D] tensor")
+    dt = _dtype_of(q)
+    R, H, D = q.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 2:
+        raise PivotError("k must be a [Lk, D] tensor")
+    Lk = k.shape[0]
+    _expect(w, "w", (R, H), torch.float32)
+    _expect(k, "k", (Lk, D), q.dtype)
+    _scales(dt, q_scale, k_scale, (R,), (Lk,))
+    _on_device(q=q, w=w, k=k, q_scale=q_scale, k_scale=k_scale)
+    row_end = R if row_end is None else row_end
+    S = torch.full((max(row_end - row_begin, 0), Lk), float("nan"), dtype=torch.float32,
+                   device=q.device)
+    _check(L.pivot_dbg_score_rows(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), R, Lk,
+                                  H, D, dt, row_begin, row_end, pos_mul, pos_add, _ptr(S), Lk,
+                                  _stream(stream)))
+    return S
+
+
+def _decode_inputs(q, w, k_cache, cache_len, q_scale, k_scale):
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise PivotError("q must be a [B, g, H, D] tensor")
+    dt = _dtype_of(q)
+    B, g, H, D = q.shape
+    if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 3:
+        raise PivotError("k_cache must be a [B, Lmax, D] tensor")
+    Lmax = k_cache.shape[1]
+    _expect(w, "w", (B, g, H), torch.float32)
+    _expect(k_cache, "k_cache", (B, Lmax, D), q.dtype)
+    _expect(cache_len, "cache_len", (B,), torch.int32)
+    _scales(dt, q_scale, k_scale, (B, g), (B, Lmax))
+    return dt, B, g, H, D, Lmax
+
+
 def indexer_decode(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="refine",
                    q_scale=None, k_scale=None, out=None, workspace=None,
-                   stream=None, window: int = 0, window_mode="shared") -> torch.Tensor:
+                   stream=None, window: int = 0, window_mode="shared", out_scores=None,
+                   return_scores: bool = False):
     """One MTP decode step: q [B,g,H,D], w [B,g,H], k_cache [B,Lmax,D],
     cache_len [B] int32 (device); fp8 needs q_scale [B,g], k_scale [B,Lmax].
-    Returns int32 [B, g, topk] ([B, g, topk + window] with a window)."""
+    Returns int32 [B, g, topk] ([B, g, topk + window] with a window); with
+    return_scores (no window) also the float32 [B, g, topk] scores."""
     L = load()
-    q, w, k_cache = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k_cache, "k_cache")
-    cache_len = _dev(cache_len, "cache_len", torch.int32)
-    B, g, H, D = q.shape
-    Lmax = k_cache.shape[1]
-    dt = _dtype_of(q)
+    dt, B, g, H, D, Lmax = _decode_inputs(q, w, k_cache, cache_len, q_scale, k_scale)
     m = _mode(mode)
-    if out is None:
-        out = torch.empty((B, g, topk + window), dtype=torch.int32, device=q.device)
+    if window < 0:
+        raise PivotError("window must be >= 0")
+    wm = _window_mode(window_mode)
+    out = _out(out, "out", (B, g, topk + window), torch.int32, q.device)
+    want = return_scores or out_scores is not None
+    if want:
+        if window:
+            raise PivotError("scores are returned without a window only")
+        out_scores = _out(out_scores, "out_scores", (B, g, topk), torch.float32, q.device)
+    _on_device(q=q, w=w, k_cache=k_cache, cache_len=cache_len, q_scale=q_scale, k_scale=k_scale)
     ws = _workspace(L.pivot_decode_workspace_size(B, Lmax, H, D, g, topk, C, m, dt), q.device,
                     workspace)
-    nbytes = ws.numel() * ws.element_size()
+    nbytes = ws.numel()
     if window:
         _check(L.pivot_indexer_decode_window(
             _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(cache_len), B,
-            Lmax, H, D, g, topk, C, m, dt, window, _window_mode(window_mode), _ptr(out), _ptr(ws),
-            nbytes, _stream(stream)))
+            Lmax, H, D, g, topk, C, m, dt, window, wm, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
     else:
         _check(L.pivot_indexer_decode(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache),
                                       _ptr(k_scale), _ptr(cache_len), B, Lmax, H, D, g, topk, C, m,
-                                      dt, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
-    return out
+                                      dt, _ptr(out), _ptr(out_scores), _ptr(ws), nbytes,
+                                      _stream(stream)))
+    return (out, out_scores) if want else out
 
 
 def indexer_decode_paged(q, w, k_pages, block_table, cache_len, *, topk: int, C: int = 0,
@@ -303,23 +426,32 @@ def indexer_decode_paged(q, w, k_pages, block_table, cache_len, *, topk: int, C:
     page_size].  Other arguments as for indexer_decode.  Returns int32
     [B, g, topk + window]."""
     L = load()
-    q, w, k_pages = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k_pages, "k_pages")
-    block_table = _dev(block_table, "block_table", torch.int32)
-    cache_len = _dev(cache_len, "cache_len", torch.int32)
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise PivotError("q must be a [B, g, H, D] tensor")
+    dt = _dtype_of(q)
     B, g, H, D = q.shape
+    if not isinstance(k_pages, torch.Tensor) or k_pages.dim() != 3:
+        raise PivotError("k_pages must be a [num_pages, page_size, D] tensor")
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2:
+        raise PivotError("block_table must be a [B, max_pages] tensor")
     num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
     max_pages = block_table.shape[1]
-    dt = _dtype_of(q)
+    _expect(w, "w", (B, g, H), torch.float32)
+    _expect(k_pages, "k_pages", (num_pages, page_size, D), q.dtype)
+    _expect(block_table, "block_table", (B, max_pages), torch.int32)
+    _expect(cache_len, "cache_len", (B,), torch.int32)
+    _scales(dt, q_scale, k_scale, (B, g), (num_pages, page_size))
+    _on_device(q=q, w=w, k_pages=k_pages, block_table=block_table, cache_len=cache_len,
+               q_scale=q_scale, k_scale=k_scale)
     m = _mode(mode)
-    if out is None:
-        out = torch.empty((B, g, topk + window), dtype=torch.int32, device=q.device)
+    wm = _window_mode(window_mode)
+    out = _out(out, "out", (B, g, topk + window), torch.int32, q.device)
     ws = _workspace(L.pivot_decode_workspace_size(B, max_pages * page_size, H, D, g, topk, C, m, dt),
                     q.device, workspace)
     _check(L.pivot_indexer_decode_paged(
         _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_pages), _ptr(k_scale), num_pages, page_size,
-        _ptr(block_table), max_pages, _ptr(cache_len), B, H, D, g, topk, C, m, dt, window,
-        _window_mode(window_mode), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-        _stream(stream)))
+        _ptr(block_table), max_pages, _ptr(cache_len), B, H, D, g, topk, C, m, dt, window, wm,
+        _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
@@ -327,19 +459,15 @@ def decode_candidates(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="
                       q_scale=None, k_scale=None, workspace=None, stream=None) -> torch.Tensor:
     """Every sequence's proxy top-m for one decode step: int32 [B, m]."""
     L = load()
-    q, w, k_cache = _dev(q, "q"), _dev(w, "w", torch.float32), _dev(k_cache, "k_cache")
-    cache_len = _dev(cache_len, "cache_len", torch.int32)
-    B, g, H, D = q.shape
-    Lmax = k_cache.shape[1]
-    dt = _dtype_of(q)
+    dt, B, g, H, D, Lmax = _decode_inputs(q, w, k_cache, cache_len, q_scale, k_scale)
     m = _mode(mode)
+    _on_device(q=q, w=w, k_cache=k_cache, cache_len=cache_len, q_scale=q_scale, k_scale=k_scale)
     cand = torch.empty((B, C if m == REFINE else topk), dtype=torch.int32, device=q.device)
     ws = _workspace(L.pivot_decode_workspace_size(B, Lmax, H, D, g, topk, C, m, dt), q.device,
                     workspace)
     _check(L.pivot_decode_candidates(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache),
                                      _ptr(k_scale), _ptr(cache_len), B, Lmax, H, D, g, topk, C,
-                                     m, dt, _ptr(cand), _ptr(ws), ws.numel() * ws.element_size(),
-                                     _stream(stream)))
+                                     m, dt, _ptr(cand), _ptr(ws), ws.numel(), _stream(stream)))
     return cand
 
 
@@ -353,28 +481,41 @@ def sparse_attention(q, k, v, idx, *, rows_per_seq: Optional[int] = None, seq_le
     [R,Hq,dv]."""
     import math
     L = load()
-    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
-    idx = _dev(idx, "idx", torch.int32)
+    if not isinstance(q, torch.Tensor) or q.dim() != 3 or q.dtype != torch.bfloat16:
+        raise PivotError("q must be a bf16 [R, Hq, d] tensor")
     R, Hq, d = q.shape
+    if not isinstance(k, torch.Tensor) or not isinstance(v, torch.Tensor) or k.dim() != v.dim() \
+            or k.dim() not in (2, 3):
+        raise PivotError("k and v must both be [N, d] / [N, dv] or [B, S, d] / [B, S, dv] tensors")
     dv = v.shape[-1]
+    _expect(k, "k", tuple(k.shape[:-1]) + (d,), torch.bfloat16)
+    _expect(v, "v", tuple(k.shape[:-1]) + (dv,), torch.bfloat16)
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 2:
+        raise PivotError("idx must be a [R, nidx] tensor")
+    _expect(idx, "idx", (R, idx.shape[1]), torch.int32)
     if k.dim() == 2:
         stride, nkeys = 0, k.shape[0]
         rows_per_seq = R if rows_per_seq is None else rows_per_seq
     else:
         stride, nkeys = k.shape[1], k.shape[1]
         if rows_per_seq is None:
-            raise ValueError("rows_per_seq is needed with per-sequence k/v")
+            raise PivotError("rows_per_seq is needed with per-sequence k/v")
+        if (R + rows_per_seq - 1) // rows_per_seq > k.shape[0]:
+            raise PivotError(f"{R} rows of {rows_per_seq} per sequence need more than {k.shape[0]} sequences")
     seq_len = nkeys if seq_len is None else seq_len
+    if seq_len > nkeys:
+        raise PivotError(f"seq_len={seq_len} exceeds the {nkeys} key rows per sequence")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     nidx = idx.shape[1]
-    if out is None:
-        out = torch.empty((R, Hq, dv), dtype=torch.float32, device=q.device)
+    if out is not None:
+        _expect(out, "out", (R, Hq, dv), torch.float32)
+    _on_device(q=q, k=k, v=v, idx=idx)
+    out = _out(out, "out", (R, Hq, dv), torch.float32, q.device)
     need = L.pivot_sparse_attention_workspace_size(R, Hq, dv, nidx)
     ws = _workspace(need, q.device, workspace) if need else None
     _check(L.pivot_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), R, Hq, d, dv, nidx,
                                     rows_per_seq, stride, seq_len, float(scale), _ptr(out),
-                                    _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                                    _stream(stream)))
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return out
 
 

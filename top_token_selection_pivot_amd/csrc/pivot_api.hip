@@ -106,9 +106,10 @@ int validate_common(const void* q, const float* q_scale, const float* w, const v
   if (!q || !w || !k) return fail(PIVOT_ERR_NULL, "q, w and k must be non-NULL");
   if (dtype == PIVOT_FP8_E4M3 && (!q_scale || !k_scale))
     return fail(PIVOT_ERR_NULL, "fp8 inputs need q_scale and k_scale");
-  if (H < 1 || H > 64) return fail(PIVOT_ERR_SHAPE, "H=%d outside 1..64", H);
+  if (H < 1) return fail(PIVOT_ERR_SHAPE, "H=%d must be >= 1", H);
+  if (H > 64) return fail(PIVOT_ERR_UNSUPPORTED, "H=%d: the kernels hold at most 64 heads", H);
   if (!score_shape_supported(dtype, D))
-    return fail(PIVOT_ERR_SHAPE, "D=%d unsupported for %s", D, dtype == PIVOT_BF16 ? "bf16" : "fp8");
+    return fail(PIVOT_ERR_UNSUPPORTED, "D=%d unsupported for %s", D, dtype == PIVOT_BF16 ? "bf16" : "fp8");
   if (g < 1) return fail(PIVOT_ERR_PARAM, "g=%d must be >= 1", g);
   if (topk < 1) return fail(PIVOT_ERR_PARAM, "topk=%d must be >= 1", topk);
   if (mode == PIVOT_MODE_REFINE && C < topk)
@@ -189,10 +190,12 @@ struct ProfileScope {
 
 // Runs the prefill path.  `cand_user` (optional) receives every group's top-m
 // and skips the member step (pivot_candidates).
+// `outs` (optional, no window) receives the score of every output entry.
 int run_prefill(const void* q, const float* q_scale, const float* w, const void* k,
                 const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
                 int dtype, int32_t* out, int32_t* cand_user, void* workspace,
-                size_t workspace_bytes, void* stream, int window = 0, int wmode = 0) {
+                size_t workspace_bytes, void* stream, int window = 0, int wmode = 0,
+                float* outs = nullptr) {
   int st = validate_common(q, q_scale, w, k, k_scale, H, D, g, topk, C, mode, dtype);
   if (st) return st;
   st = validate_window(window, wmode, topk);
@@ -205,8 +208,9 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
   if ((long long)L * D * esize(dtype) >= (1ll << 31))
     return fail(PIVOT_ERR_SHAPE, "the key array (L*D codes) must stay below 2 GiB");
   if (!out && !cand_user) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
-  if ((out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)))
+  if ((out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)) || (outs && !aligned(outs, 4)))
     return fail(PIVOT_ERR_ALIGN, "output must be 4-byte aligned");
+  if (outs && window > 0) return fail(PIVOT_ERR_INTERNAL, "scores are written without a window only");
   if (!workspace) return fail(PIVOT_ERR_NULL, "workspace must be non-NULL");
   if (!aligned(workspace, kAlign)) return fail(PIVOT_ERR_ALIGN, "workspace must be 256-byte aligned");
   const bool dense = mode == PIVOT_MODE_DENSE;
@@ -263,6 +267,10 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
       ta.m = topk;
       ta.out = out + (size_t)r0 * ldo;
       ta.ldo = ldo;
+      if (outs) {
+        ta.out_s = outs + (size_t)r0 * topk;
+        ta.ldos = topk;
+      }
       PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_topk(ta, s), "dense top-k");
       continue;
     }
@@ -276,6 +284,12 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
     if (mode == PIVOT_MODE_REUSE) {
       BroadcastArgs ba{cdst, p.m, r0, out + (size_t)row_begin * ldo, topk, 0, g, 0, nullptr,
                        row_begin, row_end, ldo, excl};
+      if (outs) {  // the proxy's scores of this pass are still in S
+        ba.S = S;
+        ba.ldS = p.ldS;
+        ba.out_s = outs + (size_t)row_begin * topk;
+        ba.ldos = topk;
+      }
       PIVOT_LAUNCH_K(PIVOT_K_BROADCAST, s, launch_broadcast(ba, s), "reuse broadcast");
     } else {
       RefineArgs ra{qb, q_scale, w, kb, k_scale, H, 0, L, g, 0, nullptr, r0, r1, cdst, p.m, p.m,
@@ -296,6 +310,10 @@ int run_prefill(const void* q, const float* q_scale, const float* w, const void*
       tr.map = cdst;
       tr.ldmap = p.m;
       tr.map_grp_begin = r0;
+      if (outs) {
+        tr.out_s = outs + (size_t)row_begin * topk;
+        tr.ldos = topk;
+      }
       PIVOT_LAUNCH_K(PIVOT_K_MEMBER_SELECT, s, launch_topk(tr, s), "refine top-k");
     }
   }
@@ -364,16 +382,18 @@ const char* pivot_status_string(int status) {
   switch (status) {
     case PIVOT_OK: return "ok";
     case PIVOT_ERR_NULL: return "null pointer";
-    case PIVOT_ERR_SHAPE: return "unsupported shape";
+    case PIVOT_ERR_SHAPE: return "invalid shape";
     case PIVOT_ERR_PARAM: return "invalid parameter";
+    case PIVOT_ERR_UNSUPPORTED: return "unsupported shape";
     case PIVOT_ERR_ALIGN: return "misaligned pointer";
     case PIVOT_ERR_WORKSPACE: return "workspace too small";
     case PIVOT_ERR_HIP: return "HIP launch failure";
+    case PIVOT_ERR_INTERNAL: return "internal error";
     default: return "unknown status";
   }
 }
 
-const char* pivot_last_error(void) { return g_err; }
+const char* pivot_last_error_detail(void) { return g_err; }
 
 size_t pivot_workspace_size(int L, int H, int D, int g, int topk, int C, int mode, int dtype) {
   if (L < 1 || H < 1 || D < 1 || g < 1 || topk < 1) return 0;
@@ -395,10 +415,11 @@ size_t pivot_workspace_min_size(int L, int H, int D, int g, int topk, int C, int
 
 int pivot_indexer(const void* q, const float* q_scale, const float* w, const void* k,
                   const float* k_scale, int L, int H, int D, int g, int topk, int C, int mode,
-                  int dtype, int32_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+                  int dtype, int32_t* out, float* out_scores, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
   return run_prefill(q, q_scale, w, k, k_scale, L, H, D, g, topk, C, mode, dtype, out, nullptr,
-                     workspace, workspace_bytes, stream);
+                     workspace, workspace_bytes, stream, 0, 0, out_scores);
 }
 
 size_t pivot_varlen_workspace_size(const int64_t* cu_seqlens, int nseq, int H, int D, int g, int topk,
@@ -526,7 +547,7 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
                       int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
                       int dtype, int32_t* out, int32_t* cand_user, void* workspace,
                       size_t workspace_bytes, void* stream, int window = 0, int wmode = 0,
-                      const PagedKeys* pk = nullptr) {
+                      const PagedKeys* pk = nullptr, float* outs = nullptr) {
   int st = validate_common(q, q_scale, w, k_cache, k_scale, H, D, g, topk, C, mode, dtype);
   if (st) return st;
   st = validate_window(window, wmode, topk);
@@ -541,8 +562,10 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
     return fail(PIVOT_ERR_SHAPE, "one sequence's key cache (Lmax*D codes) must stay below 2 GiB");
   if (!cache_len || (!out && !cand_user) || !workspace)
     return fail(PIVOT_ERR_NULL, "cache_len, out and workspace must be non-NULL");
-  if (!aligned(cache_len, 4) || (out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)))
+  if (!aligned(cache_len, 4) || (out && !aligned(out, 4)) || (cand_user && !aligned(cand_user, 4)) ||
+      (outs && !aligned(outs, 4)))
     return fail(PIVOT_ERR_ALIGN, "cache_len and outputs must be 4-byte aligned");
+  if (outs && window > 0) return fail(PIVOT_ERR_INTERNAL, "scores are written without a window only");
   if (!aligned(workspace, kAlign)) return fail(PIVOT_ERR_ALIGN, "workspace must be 256-byte aligned");
   const DecodePlan p = plan_decode(B, Lmax, H, D, g, topk, C, mode, dtype);
   if (workspace_bytes < p.total)
@@ -570,6 +593,8 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
     sel.kind = kLenDecodeDense;
     sel.out = out;
     sel.ldo = ldo;
+    sel.out_s = outs;
+    sel.ldos = topk;
     PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_decode_select(sel, s), "decode dense top-k");
     if (window > 0) PIVOT_LAUNCH_K(PIVOT_K_WINDOW, s, launch_window_union(wa, s), "window union");
     return PIVOT_OK;
@@ -592,6 +617,12 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   if (cand_user) return PIVOT_OK;
   if (mode == PIVOT_MODE_REUSE) {
     BroadcastArgs ba{cand, p.m, 0, out, topk, 1, g, Lmax, cache_len, 0, B * g, ldo, excl};
+    if (outs) {
+      ba.S = S;
+      ba.ldS = p.ldS;
+      ba.out_s = outs;
+      ba.ldos = topk;
+    }
     PIVOT_LAUNCH_K(PIVOT_K_BROADCAST, s, launch_broadcast(ba, s), "decode reuse broadcast");
     if (window > 0) PIVOT_LAUNCH_K(PIVOT_K_WINDOW, s, launch_window_union(wa, s), "window union");
     return PIVOT_OK;
@@ -623,6 +654,8 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
   tr.map = cand;
   tr.ldmap = p.m;
   tr.map_grp_begin = 0;
+  tr.out_s = outs;
+  tr.ldos = topk;
   PIVOT_LAUNCH_K(PIVOT_K_MEMBER_SELECT, s, launch_topk(tr, s), "decode refine top-k");
   if (window > 0) PIVOT_LAUNCH_K(PIVOT_K_WINDOW, s, launch_window_union(wa, s), "window union");
   return PIVOT_OK;
@@ -631,11 +664,11 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
 int pivot_indexer_decode(const void* q, const float* q_scale, const float* w,
                          const void* k_cache, const float* k_scale, const int32_t* cache_len,
                          int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
-                         int dtype, int32_t* out, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         int dtype, int32_t* out, float* out_scores, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
   return run_decode(q, q_scale, w, k_cache, k_scale, cache_len, B, Lmax, H, D, g, topk, C, mode,
-                    dtype, out, nullptr, workspace, workspace_bytes, stream);
+                    dtype, out, nullptr, workspace, workspace_bytes, stream, 0, 0, nullptr, out_scores);
 }
 
 int pivot_indexer_window(const void* q, const float* q_scale, const float* w, const void* k,
@@ -683,6 +716,37 @@ int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,
                     dtype, nullptr, cand, workspace, workspace_bytes, stream);
 }
 
+int pivot_dbg_score_rows(const void* q, const float* q_scale, const float* w, const void* k,
+                         const float* k_scale, int R, int Lk, int H, int D, int dtype, int row_begin,
+                         int row_end, int pos_mul, int pos_add, float* S, long long ldS, void* stream) {
+  int st = validate_common(q, q_scale, w, k, k_scale, H, D, 1, 1, 1, PIVOT_MODE_DENSE, dtype);
+  if (st) return st;
+  if (R < 1 || Lk < 1) return fail(PIVOT_ERR_SHAPE, "R=%d and Lk=%d must be >= 1", R, Lk);
+  if ((long long)Lk * D * esize(dtype) >= (1ll << 31))
+    return fail(PIVOT_ERR_SHAPE, "the key array (Lk*D codes) must stay below 2 GiB");
+  if (row_begin < 0 || row_end > R || row_begin > row_end)
+    return fail(PIVOT_ERR_SHAPE, "rows [%d, %d) must lie in [0, %d)", row_begin, row_end, R);
+  if (pos_mul < 0) return fail(PIVOT_ERR_PARAM, "pos_mul=%d must be >= 0", pos_mul);
+  if (!S) return fail(PIVOT_ERR_NULL, "S must be non-NULL");
+  if (!aligned(S, 4)) return fail(PIVOT_ERR_ALIGN, "S must be 4-byte aligned");
+  if (row_begin == row_end) return PIVOT_OK;
+  const long long plast = std::min<long long>((long long)(row_end - 1) * pos_mul + pos_add, Lk - 1);
+  if (ldS < plast + 1) return fail(PIVOT_ERR_PARAM, "ldS=%lld is below the last row's %lld scores", ldS, plast + 1);
+  if ((long long)row_end * pos_mul + pos_add > INT32_MAX)
+    return fail(PIVOT_ERR_PARAM, "row positions overflow");
+  hipStream_t s = (hipStream_t)stream;
+  const ScanArgs sa{(const uint8_t*)q, q_scale, w, (const uint8_t*)k, k_scale, Lk, H, row_begin, row_end,
+                    pos_mul, pos_add, Lk - 1, kScanKeyChunk, S, ldS};
+  for (int rs = row_begin; rs < row_end; rs += kScanRowsPerLaunch) {
+    ScanArgs sb = sa;
+    sb.row_begin = rs;
+    sb.row_end = std::min(row_end, rs + kScanRowsPerLaunch);
+    sb.S = S + (size_t)(rs - row_begin) * ldS;
+    PIVOT_LAUNCH_K(PIVOT_K_SCAN, s, launch_scan(sb, dtype, D, s), "score rows");
+  }
+  return PIVOT_OK;
+}
+
 // Sparse main attention: chunks per row.  Many rows: one chunk each (no
 // merge); few rows: chunks of kSAttnChunk slots so that about 1024 waves run.
 constexpr int kSAttnChunk = 128;
@@ -714,7 +778,7 @@ int pivot_sparse_attention(const void* q, const void* k, const void* v, const in
   if (!q || !k || !v || !idx || !out) return fail(PIVOT_ERR_NULL, "q, k, v, idx and out must be non-NULL");
   if (R < 1 || nidx < 1) return fail(PIVOT_ERR_SHAPE, "R=%d and nidx=%d must be >= 1", R, nidx);
   if (!sattn_shape_supported(Hq, d, dv))
-    return fail(PIVOT_ERR_SHAPE, "sparse attention supports d = dv = 128 and Hq in {32, 64} (got %d, %d, %d)", d,
+    return fail(PIVOT_ERR_UNSUPPORTED, "sparse attention supports d = dv = 128 and Hq in {32, 64} (got %d, %d, %d)", d,
                 dv, Hq);
   if (rows_per_seq < 1 || seq_len < 0 || seq_stride < 0)
     return fail(PIVOT_ERR_PARAM, "rows_per_seq=%d must be >= 1, seq_len=%d and seq_stride=%lld >= 0", rows_per_seq,

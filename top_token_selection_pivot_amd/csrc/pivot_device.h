@@ -86,7 +86,11 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // LDS byte address lds + 16*l (4*l); reads past the buffer's range write zeros.
 // They are issued as inline assembly, outside the compiler's wait tracking, so
 // the caller waits for them explicitly (lds_dma_wait) before reading the
-// destination.  Nothing else in the kernels that use them reads M0.
+// destination.  (The compiler's own builtin for these loads makes it wait for
+// every load in flight before each later LDS atomic, which would drain the
+// rings.)  The LDS address goes through M0, a register the compiler reserves:
+// each statement saves M0 in a scratch SGPR and restores it afterwards, so the
+// compiler's view of M0 is never invalidated.
 //
 // The buffer descriptor of these loads: base address, no stride, `bytes` of
 // range, raw-buffer flags; every word made wave-uniform so it lives in SGPRs.
@@ -97,16 +101,22 @@ __device__ inline i32x4 dma_rsrc(const void* base, uint32_t bytes, int flags) {
                __builtin_amdgcn_readfirstlane((int)bytes), flags};
 }
 __device__ inline void lds_dma16(i32x4 rsrc, uint32_t lds, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
-               : "memory");
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
+      : "memory");
 }
 __device__ inline void lds_dma4(i32x4 rsrc, uint32_t lds, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
-               : "memory");
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rsrc)
+      : "memory");
 }
 // Wait until at most N vector-memory operations of the wave are outstanding
 // (they complete in issue order); a compiler barrier for memory accesses.
@@ -141,6 +151,12 @@ __device__ inline uint32_t score_key(float f) {
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// The score a key stands for (the inverse of score_key; -0 comes back as +0).
+__device__ inline float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+// The value written where an output position is -1.
+__device__ inline float no_score() { return __uint_as_float(0x7FC00000u); }
 
 // ---------------------------------------------------------------------------
 // Storage codecs used by the proxy step.

@@ -118,6 +118,8 @@ struct DecSelectArgs {
   long long ldo;
   int excl = 0;  // window excluded: row lengths shrink by excl
   uint32_t* thr = nullptr;  // per row: first-digit threshold bin, keys in higher bins
+  float* out_s = nullptr;   // optional: score of every output entry (NaN for -1), stride ldos
+  long long ldos = 0;
 };
 
 // Row-length rules of the top-m selection.
@@ -143,6 +145,8 @@ struct TopkArgs {
   const int32_t* map;  // kLenRefine: candidate lists
   int ldmap, map_grp_begin;
   int excl = 0;        // kLenRefine / kLenCache / kLenDecodeDense: limits move down by excl
+  float* out_s = nullptr;  // optional: score of every output entry (NaN for -1), stride ldos
+  long long ldos = 0;
 };
 
 // Reuse: member rows [row_begin, row_end) receive their group's proxy top-k
@@ -157,6 +161,12 @@ struct BroadcastArgs {
   int row_begin, row_end;
   long long ldo = 0;  // output row stride (0: topk)
   int excl = 0;       // window excluded: member t keeps entries <= t - excl
+  // optional scores: out_s[i][s] = the proxy's score S[j - grp_begin][position]
+  // (NaN for -1); S holds the proxy score rows of groups grp_begin.. (stride ldS)
+  const float* S = nullptr;
+  long long ldS = 0;
+  float* out_s = nullptr;
+  long long ldos = 0;
 };
 
 // Sliding window added in place to selected rows: row i of out (stride ldo)

@@ -329,9 +329,13 @@ __device__ inline float f4(const float4& v, int e) { return e == 0 ? v.x : e == 
 // contiguous run of the output: they are placed in LDS (`stage`, kEmitStage
 // words; any overflow is written directly) and then stored coalesced.
 constexpr int kEmitStage = kSelectBins1;
+// The score of every emitted entry also goes to the buffer `srs` (a range of
+// zero bytes when no scores are wanted, so the stores are dropped): written
+// directly, not staged -- a checking aid, not the fast path.
 template <int E, typename Get>
 __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint32_t m, const int32_t* list,
-                                     int32_t* out, uint32_t* scratch, int32_t* stage, Get get) {
+                                     int32_t* out, __amdgpu_buffer_rsrc_t srs, uint32_t* scratch, int32_t* stage,
+                                     Get get) {
   const int tid = threadIdx.x;
   const uint32_t need_gt = m - need_eq;
   uint32_t g_gt = 0, g_eq = 0;
@@ -351,8 +355,9 @@ __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint
     const uint32_t excl = block_exclusive_sum<kTopkThreads>(cgt | (ceq << 16), scratch, &tot);
     const uint32_t p0 = g_gt + min(g_eq, need_eq);  // the round's first output position
     uint32_t gt_before = g_gt + (excl & 0xFFFFu), eq_before = g_eq + (excl >> 16);
-    auto put = [&](uint32_t p, int sl) {
+    auto put = [&](uint32_t p, int sl, uint32_t k) {
       if (p >= m) return;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_score(k)), srs, (int)(p * 4), 0, 0);
       if (p - p0 < (uint32_t)kEmitStage) stage[p - p0] = sl;
       else out[p] = list ? list[sl] : sl;
     };
@@ -360,10 +365,10 @@ __device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint
     for (int e = 0; e < E; ++e) {
       if (slot[e] < 0) continue;
       if (key[e] > T) {
-        put(gt_before + min(eq_before, need_eq), slot[e]);
+        put(gt_before + min(eq_before, need_eq), slot[e], key[e]);
         ++gt_before;
       } else if (key[e] == T) {
-        if (eq_before < need_eq) put(gt_before + eq_before, slot[e]);
+        if (eq_before < need_eq) put(gt_before + eq_before, slot[e], key[e]);
         ++eq_before;
       }
     }
@@ -394,7 +399,7 @@ struct alignas(16) SelectShared {
 // digits (over the ncand keys staged in LDS in index order, or, for
 // ncand < 0, over the row in memory) and emits the selection in index order.
 __device__ __forceinline__ void select_finish(SelectShared& sm, int ncand, uint32_t b1, uint32_t rem, const float* row,
-                              int n, uint32_t m, const int32_t* list, int32_t* out) {
+                              int n, uint32_t m, const int32_t* list, int32_t* out, float* outs) {
   constexpr int NT = kTopkThreads;
   const int tid = threadIdx.x;
   uint32_t prefix = b1 << (32 - kTopkBits1);
@@ -435,9 +440,11 @@ __device__ __forceinline__ void select_finish(SelectShared& sm, int ncand, uint3
   const uint32_t T = prefix;
   const uint32_t need_eq = rem;  // keys equal to T to take, lowest positions first
   int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(outs ? (void*)outs : (void*)out, 0, outs ? (int)(m * 4) : 0, 0x00020000);
   if (ncand >= 0) {
     // four consecutive staged entries per thread: one 16-byte read each
-    emit_selected<4>(ncand, T, need_eq, m, list, out, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
+    emit_selected<4>(ncand, T, need_eq, m, list, out, srs, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
       const uint4 kv = *reinterpret_cast<const uint4*>(&sm.ckey[i0 < kTopkCap ? i0 : 0]);
       const int4 sv = *reinterpret_cast<const int4*>(&sm.cslot[i0 < kTopkCap ? i0 : 0]);
       key[0] = kv.x, key[1] = kv.y, key[2] = kv.z, key[3] = kv.w;
@@ -447,7 +454,7 @@ __device__ __forceinline__ void select_finish(SelectShared& sm, int ncand, uint3
         if (i0 + e >= ncand) slot[e] = -1;
     });
   } else {
-    emit_selected<4 * kTopkU>(n, T, need_eq, m, list, out, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
+    emit_selected<4 * kTopkU>(n, T, need_eq, m, list, out, srs, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
 #pragma unroll
       for (int e = 0; e < 4 * kTopkU; ++e) {
         const bool valid = i0 + e < n;
@@ -468,6 +475,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const int R = a.row_begin + i;
   const float* row = a.S + (long long)i * a.ldS;
   int32_t* out = a.out + (long long)i * a.ldo;
+  float* outs = a.out_s ? a.out_s + (long long)i * a.ldos : nullptr;
   const bool whole_pre = a.kind == kLenRefine && a.ldmap <= kTopkU * NT * 4;
   for (int b = tid; b < NB1; b += NT) sm.hist[b] = 0u;
   // a Refine row has at most ldmap scores: when they fit one pass-1 round
@@ -500,7 +508,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const uint32_t m = (uint32_t)a.m;
 
   if (n <= (int)m) {
-    for (int s = tid; s < (int)m; s += NT) out[s] = s < n ? (list ? list[s] : s) : -1;
+    for (int s = tid; s < (int)m; s += NT) {
+      out[s] = s < n ? (list ? list[s] : s) : -1;
+      if (outs) outs[s] = s < n ? row[s] : no_score();
+    }
     return;
   }
 
@@ -658,7 +669,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   } else {
     ncand = -1;  // fall back to passes over the row in memory
   }
-  select_finish(sm, ncand, b1, rem, row, n, m, list, out);
+  select_finish(sm, ncand, b1, rem, row, n, m, list, out, outs);
 }
 
 // ---------------------------------------------------------------------------
@@ -711,6 +722,7 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
   const int R = a.row_begin + i;
   const float* row = a.S + (long long)i * a.ldS;
   int32_t* out = a.out + (long long)i * a.ldo;
+  float* outs = a.out_s ? a.out_s + (long long)i * a.ldos : nullptr;
   const uint32_t m = (uint32_t)a.m;
   // the row (at most ldmap <= kSmallMax scores) and its candidate positions
   // are loaded up front; the row length, the number of candidates <= the
@@ -719,7 +731,10 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
   int t;
   refine_row_list(a, R, &list, &t);
   if (!list) {
-    for (int s = lane; s < (int)m; s += kWave) out[s] = -1;
+    for (int s = lane; s < (int)m; s += kWave) {
+      out[s] = -1;
+      if (outs) outs[s] = no_score();
+    }
     return;
   }
   const int lmax = a.ldmap;
@@ -749,7 +764,10 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
   wave_exclusive_sum(cnt_le, &n_u);
   const int n = (int)n_u;
   if (n <= (int)m) {
-    for (int s = lane; s < (int)m; s += kWave) out[s] = s < n ? list[s] : -1;
+    for (int s = lane; s < (int)m; s += kWave) {
+      out[s] = s < n ? list[s] : -1;
+      if (outs) outs[s] = s < n ? row[s] : no_score();
+    }
     return;
   }
   // Entries past the row get key 0.  No score has key 0 (it would be a NaN),
@@ -867,11 +885,17 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
       const uint32_t kk = key[c * 4 + e];
       if (kk > T) {
         const uint32_t p = gt_before + min(eq_before, need_eq);
-        if (p < m) out[p] = val[c * 4 + e];
+        if (p < m) {
+          out[p] = val[c * 4 + e];
+          if (outs) outs[p] = key_score(kk);
+        }
         ++gt_before;
       } else if (kk == T) {
         const uint32_t p = gt_before + eq_before;
-        if (eq_before < need_eq && p < m) out[p] = val[c * 4 + e];
+        if (eq_before < need_eq && p < m) {
+          out[p] = val[c * 4 + e];
+          if (outs) outs[p] = key_score(kk);
+        }
         ++eq_before;
       }
     }
@@ -1009,8 +1033,12 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
   const uint32_t m = (uint32_t)a.m;
   const float* row = a.S + (long long)i * a.ldS;
   int32_t* out = a.out + (long long)i * a.ldo;
+  float* outs = a.out_s ? a.out_s + (long long)i * a.ldos : nullptr;
   if (n <= (int)m) {
-    for (int s = tid; s < (int)m; s += NT) out[s] = s < n ? s : -1;
+    for (int s = tid; s < (int)m; s += NT) {
+      out[s] = s < n ? s : -1;
+      if (outs) outs[s] = s < n ? row[s] : no_score();
+    }
     return;
   }
   if (tid == 0) sh_bad = 0;
@@ -1019,7 +1047,7 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
   __syncthreads();
   const uint32_t rem = m - above;
   if (sh_bad) {
-    select_finish(sm, -1, b1, rem, row, n, m, nullptr, out);
+    select_finish(sm, -1, b1, rem, row, n, m, nullptr, out, outs);
     return;
   }
   // concatenate the slices in order: slice offsets first, then every entry
@@ -1059,7 +1087,7 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
     }
   }
   __syncthreads();
-  select_finish(sm, total, b1, rem, row, n, m, nullptr, out);
+  select_finish(sm, total, b1, rem, row, n, m, nullptr, out, outs);
 }
 
 hipError_t launch_decode_select(const DecSelectArgs& a, hipStream_t st) {
@@ -1100,9 +1128,13 @@ __global__ __launch_bounds__(256) void broadcast_kernel(BroadcastArgs a) {
   }
   const int32_t* p = a.ptop + (size_t)(j - a.grp_begin) * a.ldp;
   int32_t* out = a.out + (size_t)blockIdx.x * (a.ldo ? a.ldo : a.topk);
+  float* outs = a.out_s ? a.out_s + (size_t)blockIdx.x * a.ldos : nullptr;
+  const float* srow = a.S ? a.S + (size_t)(j - a.grp_begin) * a.ldS : nullptr;
   for (int s = threadIdx.x; s < a.topk; s += 256) {
     const int v = p[s];
-    out[s] = (v >= 0 && v <= t) ? v : -1;
+    const bool keep = v >= 0 && v <= t;
+    out[s] = keep ? v : -1;
+    if (outs) outs[s] = keep ? srow[v] : no_score();
   }
 }
 
