@@ -177,7 +177,8 @@ def test_tiny_score_rows_exact(tiny):
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_decode_scores_exact(dtype):
     """Decode on integer-valued inputs (bf16, and fp8 with unit scales): the
-    scores of every mode are exact."""
+    scores of every mode are exact, except the fp8 proxy's (Reuse), whose fresh
+    scale amax/448 is a general binary32 value."""
     print(f"case: decode scores on integer inputs, B=5, {dtype}", flush=True)
     lens = [2, 37, 1000, 999, 1500]
     dec = _decode_inputs(5, lens, g=2, H=8, D=64, Lmax=1500, dtype=dtype)
@@ -193,7 +194,13 @@ def test_decode_scores_exact(dtype):
             for i in range(2):
                 sel = out[b, i][out[b, i] >= 0]
                 ref = psc[sel] if mode == "reuse" else oracle.score_list(v, i, sel)
-                assert np.array_equal(sc[b, i][:len(sel)].astype(np.float64), ref), (mode, b, i)
+                got = sc[b, i][:len(sel)].astype(np.float64)
+                if dtype == "fp8" and mode == "reuse":
+                    # the re-quantised proxy carries a general binary32 scale: the
+                    # code sum is exact, its two scale products round once each
+                    assert np.all(np.abs(got - ref) <= 2.0 ** -22 * np.abs(ref)), (mode, b, i)
+                else:
+                    assert np.array_equal(got, ref), (mode, b, i)
                 assert np.all(np.isnan(sc[b, i][len(sel):]))
 
 
@@ -207,8 +214,7 @@ def test_float_proxy_bits(dtype):
         v = oracle.View.of(inp)
         for g in gs:
             qbar, qs, wbar = pv.proxy_mean(d["q"], d["w"], g, q_scale=d.get("q_scale"))
-            if dtype == "bf16":
-                qbar = qbar.view(torch.int16)
+            qbar = qbar.view(torch.int16) if dtype == "bf16" else qbar.view(torch.uint8)
             qbar, qs, wbar = qbar.cpu().numpy(), qs.cpu().numpy(), wbar.cpu().numpy()
             if dtype == "bf16":
                 qbar = qbar.view(np.uint16)

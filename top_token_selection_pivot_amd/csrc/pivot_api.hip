@@ -331,6 +331,7 @@ struct DecodePlan {
   int m;
   int rows;   // scored rows: B proxies, or B*g members for DENSE
   int parts;  // workgroups per row in the decode top-m gather
+  int cap;    // keys per gather slice region (a slice never holds more than its length)
   long long ldS, ldR;
   size_t off_qbar, off_qs, off_wbar, off_cand, off_S, off_R, off_hist, off_ckey, off_cslot, off_ccount,
       off_thr, total;
@@ -358,12 +359,13 @@ DecodePlan plan_decode(int B, int Lmax, int H, int D, int g, int topk, int C, in
   if (mode == PIVOT_MODE_REFINE) off = align_up(off + (size_t)B * g * p.ldR * 4);
   p.rows = dense ? B * g : B;
   p.parts = (int)std::min<long long>(32, std::max<long long>(1, (Lmax + 4095) / 4096));
+  p.cap = (int)std::min<long long>(kSelectCap, round_up((Lmax + p.parts - 1) / p.parts, 16));
   p.off_hist = off;
   off = align_up(off + (size_t)p.rows * kSelectBins1 * 4);
   p.off_ckey = off;
-  off = align_up(off + (size_t)p.rows * p.parts * kSelectCap * 4);
+  off = align_up(off + (size_t)p.rows * p.parts * p.cap * 4);
   p.off_cslot = off;
-  off = align_up(off + (size_t)p.rows * p.parts * kSelectCap * 4);
+  off = align_up(off + (size_t)p.rows * p.parts * p.cap * 4);
   p.off_ccount = off;
   off = align_up(off + (size_t)p.rows * p.parts * 4);
   p.off_thr = off;
@@ -582,6 +584,7 @@ static int run_decode(const void* q, const float* q_scale, const float* w,
                     (uint32_t*)(ws + p.off_ckey), (int32_t*)(ws + p.off_cslot), (int32_t*)(ws + p.off_ccount),
                     nullptr, 0, excl};
   sel.thr = (uint32_t*)(ws + p.off_thr);
+  sel.cap = p.cap;
   const WindowArgs wa{out, ldo, B * g, topk, window, 1, g, Lmax, cache_len, 0};
   if (mode == PIVOT_MODE_DENSE) {
     PIVOT_LAUNCH_K(PIVOT_K_SELECT, s, launch_fill_u32(hist, (size_t)p.rows * kSelectBins1, 0u, s),

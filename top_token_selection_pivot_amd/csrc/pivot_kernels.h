@@ -96,6 +96,8 @@ struct DecScanArgs {
   int num_pages = 0;
 };
 
+constexpr int kSelectCapDefault = 7680;  // keys a long-row selection stages in LDS
+
 // Top-m of decode score rows with precomputed first-digit histograms: `parts`
 // workgroups per row gather the keys at or above the threshold bin of their
 // slice into per-slice regions ([nrows][parts][kTopkCap] keys and slots,
@@ -120,6 +122,7 @@ struct DecSelectArgs {
   uint32_t* thr = nullptr;  // per row: first-digit threshold bin, keys in higher bins
   float* out_s = nullptr;   // optional: score of every output entry (NaN for -1), stride ldos
   long long ldos = 0;
+  int cap = kSelectCapDefault;  // keys each slice region of ckey / cslot holds
 };
 
 // Row-length rules of the top-m selection.
@@ -219,7 +222,7 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t launch_window_union(const WindowArgs& a, hipStream_t st);
 
 constexpr int kDecChunk = 2048;      // keys per decode-scan work item
-constexpr int kSelectCap = 7680;     // keys a long-row selection stages in LDS
+constexpr int kSelectCap = kSelectCapDefault;
 constexpr int kSelectBins1 = 4096;   // bins of the first radix digit (top 12 bits)
 
 bool score_shape_supported(int dtype, int D);

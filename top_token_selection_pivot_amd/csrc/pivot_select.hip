@@ -988,8 +988,8 @@ __global__ __launch_bounds__(kGatherThreads) void dec_gather_kernel(DecSelectArg
   }
   const int per = ((n + a.parts - 1) / a.parts + 15) / 16 * 16;
   const int lo = p * per, hi = min(n, lo + per);
-  uint32_t* rkey = a.ckey + ((size_t)i * a.parts + p) * kTopkCap;
-  int32_t* rslot = a.cslot + ((size_t)i * a.parts + p) * kTopkCap;
+  uint32_t* rkey = a.ckey + ((size_t)i * a.parts + p) * a.cap;
+  int32_t* rslot = a.cslot + ((size_t)i * a.parts + p) * a.cap;
   const float* row = a.S + (long long)i * a.ldS;
   uint32_t running = 0;
   for (int base = lo; base < hi; base += E * NT) {
@@ -1073,7 +1073,7 @@ __global__ __launch_bounds__(kTopkThreads) void dec_finalize_kernel(DecSelectArg
         const int mid = (lo + hi + 1) >> 1;
         if (sh_off[mid] <= e) lo = mid; else hi = mid - 1;
       }
-      const size_t src = ((size_t)i * a.parts + lo) * kTopkCap + (e - sh_off[lo]);
+      const size_t src = ((size_t)i * a.parts + lo) * a.cap + (e - sh_off[lo]);
       kk[u] = a.ckey[src];
       ss[u] = a.cslot[src];
     }
