@@ -134,6 +134,27 @@ int pivot_indexer_decode(const void* q, const float* q_scale, const float* w,
                          size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Allocation-free decode step, for callers that cannot allocate device
+ * memory around the call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments and result as
+ * pivot_indexer_decode, without a workspace: the scratch memory is a device
+ * array inside this library, pivot_noalloc_scratch_bytes() bytes (128 MiB)
+ * on every GPU the library runs on, held until the process ends.  A step
+ * whose pivot_decode_workspace_size exceeds it returns PIVOT_ERR_WORKSPACE
+ * (the decode workload of 32 sequences of up to 131072 fp8 keys with g = 2
+ * fits in every mode).  The call uses the current device's copy (the stream
+ * must belong to the current device); it allocates and frees nothing, and
+ * every call clears what has to start at zero.  All calls on one GPU share
+ * that GPU's array, so calls that overlap on one GPU (different streams or
+ * threads without ordering) race: order them on one stream.
+ * ------------------------------------------------------------------------- */
+int pivot_indexer_decode_noalloc(const void* q, const float* q_scale, const float* w,
+                                 const void* k_cache, const float* k_scale, const int32_t* cache_len,
+                                 int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
+                                 int dtype, int32_t* out, float* out_scores, void* stream);
+size_t pivot_noalloc_scratch_bytes(void);
+
+/* ---------------------------------------------------------------------------
  * Prefill and decode with a sliding window added to every query's selection
  * (tutorial "Sparse Attention의 Indexer", section on combining the recent
  * window with the selected positions, Figure 3).  The window of size `window`

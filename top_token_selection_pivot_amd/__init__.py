@@ -75,6 +75,10 @@ def load():
     L.pivot_decode_workspace_size.argtypes = [i] * 9
     L.pivot_indexer_decode.restype = i
     L.pivot_indexer_decode.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, fp, vp, sz, vp]
+    L.pivot_indexer_decode_noalloc.restype = i
+    L.pivot_indexer_decode_noalloc.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, fp, vp]
+    L.pivot_noalloc_scratch_bytes.restype = sz
+    L.pivot_noalloc_scratch_bytes.argtypes = []
     L.pivot_dbg_score_rows.restype = i
     L.pivot_dbg_score_rows.argtypes = [vp, fp, fp, vp, fp] + [i] * 9 + [fp, C.c_longlong, vp]
     L.pivot_indexer_window.restype = i
@@ -412,6 +416,31 @@ def indexer_decode(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="ref
                                       dt, _ptr(out), _ptr(out_scores), _ptr(ws), nbytes,
                                       _stream(stream)))
     return (out, out_scores) if want else out
+
+
+def indexer_decode_noalloc(q, w, k_cache, cache_len, *, topk: int, C: int = 0, mode="refine",
+                           q_scale=None, k_scale=None, out=None, out_scores=None, stream=None):
+    """One MTP decode step through pivot_indexer_decode_noalloc: the library
+    uses its own per-GPU scratch array and allocates nothing (arguments as
+    for indexer_decode; out / out_scores may be passed in so that this
+    function allocates nothing either).  Returns out, or (out, out_scores)
+    when out_scores is given."""
+    L = load()
+    dt, B, g, H, D, Lmax = _decode_inputs(q, w, k_cache, cache_len, q_scale, k_scale)
+    m = _mode(mode)
+    out = _out(out, "out", (B, g, topk), torch.int32, q.device)
+    if out_scores is not None:
+        _expect(out_scores, "out_scores", (B, g, topk), torch.float32)
+        _dev(out_scores, "out_scores")
+    _on_device(q=q, w=w, k_cache=k_cache, cache_len=cache_len, q_scale=q_scale, k_scale=k_scale)
+    _check(L.pivot_indexer_decode_noalloc(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale),
+                                          _ptr(cache_len), B, Lmax, H, D, g, topk, C, m, dt, _ptr(out),
+                                          _ptr(out_scores), _stream(stream)))
+    return out if out_scores is None else (out, out_scores)
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().pivot_noalloc_scratch_bytes())
 
 
 def indexer_decode_paged(q, w, k_pages, block_table, cache_len, *, topk: int, C: int = 0,

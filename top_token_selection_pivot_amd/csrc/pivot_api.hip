@@ -707,6 +707,59 @@ int pivot_indexer_decode_paged(const void* q, const float* q_scale, const float*
                     mode, dtype, out, nullptr, workspace, workspace_bytes, stream, window, window_mode, &pk);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free decode step.  Its scratch memory is this device array (one
+// copy per GPU, held until the process ends); host code only ever uses the
+// device address hipGetSymbolAddress returns for the current GPU.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device (looked up once per device).
+int scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PIVOT_ERR_UNSUPPORTED, "device %d: the allocation-free entry point tracks devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PIVOT_ERR_INTERNAL, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PIVOT_OK;
+}
+}  // namespace
+
+int pivot_indexer_decode_noalloc(const void* q, const float* q_scale, const float* w, const void* k_cache,
+                                 const float* k_scale, const int32_t* cache_len, int B, int Lmax, int H, int D,
+                                 int g, int topk, int C, int mode, int dtype, int32_t* out, float* out_scores,
+                                 void* stream) {
+  if (!out) return fail(PIVOT_ERR_NULL, "out must be non-NULL");
+  void* ws = nullptr;
+  int st = scratch_of_current_device(&ws);
+  if (st) return st;
+  st = run_decode(q, q_scale, w, k_cache, k_scale, cache_len, B, Lmax, H, D, g, topk, C, mode, dtype, out,
+                  nullptr, ws, kNoAllocScratchBytes, stream, 0, 0, nullptr, out_scores);
+  if (st == PIVOT_ERR_WORKSPACE)
+    return fail(PIVOT_ERR_WORKSPACE,
+                "this decode step needs %zu bytes of scratch; the allocation-free entry point holds %zu",
+                pivot_decode_workspace_size(B, Lmax, H, D, g, topk, C, mode, dtype), kNoAllocScratchBytes);
+  return st;
+}
+
+size_t pivot_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
 int pivot_decode_candidates(const void* q, const float* q_scale, const float* w,
                             const void* k_cache, const float* k_scale, const int32_t* cache_len,
                             int B, int Lmax, int H, int D, int g, int topk, int C, int mode,
