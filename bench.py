@@ -549,6 +549,35 @@ def main():
         extras["varlen_refine_g8"] = {"lengths": lens, "ms_per_call": s_v * 1e3,
                                       "queries_per_s": 16384 / s_v}
         del out_v
+        # cross-layer index reuse stacked on the indexer: four layers of the
+        # 16K workload's shape (each its own seeded inputs), every layer full
+        # against every other layer reusing the one before it
+        layer_in = [dv_] + [upload(synth.make("dsa_prefill_16k", seed=2101 + l), torch) for l in range(3)]
+        louts = [torch.empty((16384, topk), dtype=torch.int32, device="cuda") for _ in range(4)]
+        ws_l = torch.empty(pv.workspace_size(16384, H, D, 8, topk, C, "refine", 0), dtype=torch.uint8,
+                           device="cuda")
+        ic = {"layers": 4, "workload": "dsa_prefill_16k per layer, Refine g=8"}
+        for name, full in (("all_full", [1, 1, 1, 1]), ("alternate", [1, 0, 1, 0])):
+            f = lambda full=full: pv.indexer_layers([x["q"] for x in layer_in], [x["w"] for x in layer_in],
+                                                    [x["k"] for x in layer_in], full=full, g=8, topk=topk, C=C,
+                                                    mode="refine", outs=louts, workspace=ws_l)
+            s = time_steps(f, 10, 3, torch)
+            ic[name] = {"full": full, "ms_per_step": s * 1e3}
+        pv.profile_enable(True)
+        pv.profile_read()
+        pv.indexer_layers([x["q"] for x in layer_in], [x["w"] for x in layer_in], [x["k"] for x in layer_in],
+                          full=[1, 0, 1, 0], g=8, topk=topk, C=C, mode="refine", outs=louts, workspace=ws_l)
+        torch.cuda.synchronize()
+        lp = pv.profile_read()
+        pv.profile_enable(False)
+        cms, cn = lp["layer_copy"]
+        ic["copy_kernel_us"] = cms / max(1, cn) * 1e3
+        ic["copy_kernel_GBs"] = 2 * 16384 * topk * 4 / (cms / max(1, cn) / 1e3) / 1e9
+        ic["speedup"] = ic["all_full"]["ms_per_step"] / ic["alternate"]["ms_per_step"]
+        extras["index_cache_16k"] = ic
+        log(f"index reuse, 4 layers of 16K: all full {ic['all_full']['ms_per_step']:.2f} ms, "
+            f"alternate {ic['alternate']['ms_per_step']:.2f} ms; copy {ic['copy_kernel_GBs']:.0f} GB/s")
+        del layer_in, louts, ws_l
         # the other prefill workloads, one sequence each: 16K bf16 (dense,
         # Reuse, Refine) and 64K fp8 (Reuse, Refine)
         other = {"dsa_prefill_16k": measure_prefill(torch, pv, dv_, 16384, ("dense", "reuse", "refine"),

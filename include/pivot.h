@@ -238,6 +238,39 @@ int pivot_indexer_varlen(const void* q, const float* q_scale, const float* w, co
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Cross-layer index reuse stacked on the indexer (molayo1419.me "PIVOT
+ * explained", section Try it now and the Sources list: IndexCache,
+ * "Accelerating Sparse Attention via Cross-Layer Index Reuse", stacked on
+ * PIVOT; only the title is on the pages).  A model has nlayers layers, each
+ * with its own indexer inputs.  A layer with full[l] != 0 runs the indexer
+ * (as pivot_indexer / pivot_indexer_decode, in the given mode); every other
+ * layer reuses the index rows of the nearest full layer before it, so layer
+ * 0 must be full.  Reusing layers skip their indexer entirely; their rows
+ * are copied from the source layer unless the caller passes the same out
+ * pointer for both (then nothing is written for the reusing layer).
+ *
+ *   full        [nlayers] int32, HOST memory
+ *   q, q_scale, w, k (k_cache), k_scale, out
+ *               HOST arrays of nlayers DEVICE pointers, each laid out as for
+ *               pivot_indexer (prefill) or pivot_indexer_decode (decode);
+ *               entries of reusing layers other than out are not read
+ *               (q_scale / k_scale arrays may be NULL for bf16)
+ *   cache_len   decode: one [B] array shared by every layer (device)
+ * Every full layer is validated before anything is enqueued; the layers then
+ * run in order on `stream`, sharing one workspace of pivot_workspace_size
+ * (pivot_decode_workspace_size) bytes.
+ * ------------------------------------------------------------------------- */
+int pivot_indexer_layers(int nlayers, const int32_t* full, const void* const* q, const float* const* q_scale,
+                         const float* const* w, const void* const* k, const float* const* k_scale, int L, int H,
+                         int D, int g, int topk, int C, int mode, int dtype, int32_t* const* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+int pivot_indexer_decode_layers(int nlayers, const int32_t* full, const void* const* q, const float* const* q_scale,
+                                const float* const* w, const void* const* k_cache, const float* const* k_scale,
+                                const int32_t* cache_len, int B, int Lmax, int H, int D, int g, int topk, int C,
+                                int mode, int dtype, int32_t* const* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sparse main attention over the selected positions (tutorial "Sparse
  * Attention의 Indexer", text after Figure 1): the main query of a row scores
  * the main keys at the positions the indexer selected and combines the values
@@ -329,7 +362,8 @@ enum {
   PIVOT_K_DECODE_SCAN = 6,  /* decode key-cache scan */
   PIVOT_K_WINDOW = 7,       /* sliding-window union */
   PIVOT_K_ATTENTION = 8,    /* sparse main attention (and its chunk merge) */
-  PIVOT_K_COUNT = 9
+  PIVOT_K_LAYER_COPY = 9,   /* index rows handed to a reusing layer */
+  PIVOT_K_COUNT = 10
 };
 int pivot_profile_enable(int on);
 int pivot_profile_read(double* ms, long long* launches, int n);

@@ -6,7 +6,9 @@ lives in pivot_oracle.c (plain single-threaded C, double accumulation); this
 file only marshals numpy arrays.
 
 Pinned functions (see tests/test_oracle_*.py): codecs, score, top-m, dense,
-proxy, Reuse, Refine, decode grouping, sliding-window union and exclusion, the paged-cache view.  Parity on realistic float inputs is
+proxy, Reuse, Refine, decode grouping, sliding-window union and exclusion, the
+paged-cache view, cross-layer index reuse (its layer bookkeeping is here, in
+Python; every full layer is the C oracle's indexer).  Parity on realistic float inputs is
 pinned only through invariants and the closed-form/worked examples.
 """
 from __future__ import annotations
@@ -237,6 +239,45 @@ def decode_seq_window(dec, b: int, topk_: int, C_: int, mode, W: int, wmode):
     sel, cand, _ = group(decode_view(dec, b), 0, n - dec.g, dec.g, topk_, C_, mode,
                          excl=W if wmode == WINDOW_EXCLUDED else 0)
     return window_union(sel, np.arange(n - dec.g, n), W), cand
+
+
+def _reuse_sources(full):
+    """For every layer, the layer whose index rows it uses: itself when it runs
+    its indexer, else the nearest such layer before it."""
+    src, last = [], None
+    for l, f in enumerate(full):
+        if f:
+            last = l
+        elif last is None:
+            raise ValueError("layer 0 must run its indexer")
+        src.append(last)
+    return src
+
+
+def index_cache_prefill(views, L: int, g: int, topk_: int, C_: int, mode, full, groups):
+    """Cross-layer index reuse stacked on the indexer (molayo1419.me "PIVOT
+    explained", Try it now and Sources: IndexCache, "Accelerating Sparse
+    Attention via Cross-Layer Index Reuse"; only the title is on the pages).
+    Reading: layer l with full[l] runs the indexer (prefill_groups, any mode)
+    on its own inputs views[l]; any other layer takes the rows of the nearest
+    full layer before it.  Returns the listed groups' rows for every layer."""
+    src = _reuse_sources(full)
+    rows = {}
+    for l, s in enumerate(src):
+        if s == l:
+            rows[l], _ = prefill_groups(views[l], L, g, topk_, C_, mode, groups)
+    return [rows[s].copy() for s in src]
+
+
+def index_cache_decode(decs, b: int, topk_: int, C_: int, mode, full):
+    """The same reuse over decode steps: decs[l] is layer l's decode step
+    (sharing the cache lengths); returns sequence b's [g, topk] rows per layer."""
+    src = _reuse_sources(full)
+    rows = {}
+    for l, s in enumerate(src):
+        if s == l:
+            rows[l], _, _ = decode_seq(decs[l], b, topk_, C_, mode)
+    return [rows[s].copy() for s in src]
 
 
 def group_rows(L: int, g: int, groups):

@@ -252,3 +252,26 @@ def test_paged_decode_validation(lib):
     # the pool must stay below 4 GiB of key codes: 2^26 keys of 64 bytes is 4 GiB
     assert f(num_pages=1 << 20, page_size=64, D=64) == ERR_SHAPE
     assert f(num_pages=(1 << 20) - 1, page_size=64, D=64) == ERR_WORKSPACE
+
+
+def test_layers_validation(lib):
+    import numpy as np
+    P = lambda n, v=FAKE: np.full(n, v, np.uint64)
+
+    def f(full, **kw):
+        fl = np.ascontiguousarray(full, np.int32)
+        n = len(full)
+        a = dict(q=P(n), w=P(n), k=P(n), out=P(n), wsb=1 << 40, C=256)
+        a.update(kw)
+        arr = {k_: (None if v is None else v.ctypes.data) for k_, v in a.items() if k_ in ("q", "w", "k", "out")}
+        return lib.pivot_indexer_layers(n, fl.ctypes.data, arr["q"], None, arr["w"], arr["k"], None, 2048, 4, 32, 4,
+                                        64, a["C"], pv.REFINE, 0, arr["out"], FAKE, a["wsb"], None)
+    assert f([0, 1]) == ERR_PARAM          # layer 0 must run its indexer
+    assert f([1, 0], out=None) == ERR_NULL
+    assert f([1, 0], q=None) == ERR_NULL
+    assert f([1, 1], out=np.array([FAKE, 0], np.uint64)) == ERR_NULL
+    assert f([1, 1], C=10) == ERR_PARAM    # a full layer's own checks
+    assert b"layer 0" in lib.pivot_last_error_detail()
+    assert f([1, 0, 1], wsb=100) == ERR_WORKSPACE
+    assert lib.pivot_indexer_layers(0, None, None, None, None, None, None, 1, 1, 32, 1, 1, 1, 0, 0, None, None, 0,
+                                    None) == ERR_SHAPE

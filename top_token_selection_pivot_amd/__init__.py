@@ -24,6 +24,7 @@ import torch
 __all__ = [
     "DENSE", "REUSE", "REFINE", "PivotError", "library_path", "load",
     "indexer", "indexer_decode", "indexer_decode_paged", "indexer_varlen", "score_rows",
+    "indexer_layers", "indexer_decode_layers", "indexer_decode_noalloc",
     "sparse_attention", "proxy_mean", "candidates", "decode_candidates",
     "workspace_size",
     "decode_workspace_size", "selftest_mfma_layout",
@@ -79,6 +80,10 @@ def load():
     L.pivot_indexer_decode_noalloc.argtypes = [vp, fp, fp, vp, fp, ip] + [i] * 9 + [ip, fp, vp]
     L.pivot_noalloc_scratch_bytes.restype = sz
     L.pivot_noalloc_scratch_bytes.argtypes = []
+    L.pivot_indexer_layers.restype = i
+    L.pivot_indexer_layers.argtypes = [i, vp, vp, vp, vp, vp, vp] + [i] * 8 + [vp, vp, sz, vp]
+    L.pivot_indexer_decode_layers.restype = i
+    L.pivot_indexer_decode_layers.argtypes = [i, vp, vp, vp, vp, vp, vp, ip] + [i] * 9 + [vp, vp, sz, vp]
     L.pivot_dbg_score_rows.restype = i
     L.pivot_dbg_score_rows.argtypes = [vp, fp, fp, vp, fp] + [i] * 9 + [fp, C.c_longlong, vp]
     L.pivot_indexer_window.restype = i
@@ -272,6 +277,99 @@ def indexer(q, w, k, *, g: int, topk: int, C: int = 0, mode="refine", q_scale=No
                                g, topk, C, m, dt, _ptr(out), _ptr(out_scores), _ptr(ws), nbytes,
                                _stream(stream)))
     return (out, out_scores) if want else out
+
+
+def _ptr_array(ts):
+    import numpy as np
+    return np.ascontiguousarray([0 if t is None else t.data_ptr() for t in ts], dtype=np.uint64)
+
+
+def _full_flags(full, nl):
+    import numpy as np
+    f = np.ascontiguousarray(np.asarray(full, dtype=np.int32).reshape(-1))
+    if f.shape[0] != nl:
+        raise PivotError(f"full must hold one flag per layer ({nl}), got {f.shape[0]}")
+    if nl < 1 or not f[0]:
+        raise PivotError("layer 0 must run its indexer (full[0] true)")
+    return f
+
+
+def indexer_layers(qs, ws, ks, *, full, g: int, topk: int, C: int = 0, mode="refine", q_scales=None,
+                   k_scales=None, outs=None, workspace=None, stream=None):
+    """Cross-layer index reuse stacked on the prefill indexer
+    (pivot_indexer_layers): per layer l the tensors qs[l] [L,H,D], ws[l]
+    [L,H], ks[l] [L,D] (fp8: q_scales[l], k_scales[l] [L]); full[l] true runs
+    the indexer, false reuses the rows of the nearest full layer before it
+    (only outs[l] is touched for such a layer, and its inputs may be None).
+    Returns the list of int32 [L, topk] rows per layer."""
+    L = load()
+    nl = len(qs)
+    f = _full_flags(full, nl)
+    if len(ws) != nl or len(ks) != nl:
+        raise PivotError("qs, ws and ks need one entry per layer")
+    q_scales = q_scales or [None] * nl
+    k_scales = k_scales or [None] * nl
+    shape = None
+    for l in range(nl):
+        if not f[l]:
+            continue
+        dt, Lq, H, D = _prefill_inputs(qs[l], ws[l], ks[l], q_scales[l], k_scales[l])
+        if shape is not None and (dt, Lq, H, D) != shape:
+            raise PivotError(f"layer {l}: every full layer needs the same code type and shape")
+        shape = (dt, Lq, H, D)
+        _on_device(q=qs[l], w=ws[l], k=ks[l], q_scale=q_scales[l], k_scale=k_scales[l])
+    dt, Lq, H, D = shape
+    m = _mode(mode)
+    dev = qs[0].device
+    outs = outs or [None] * nl
+    outs = [_out(o, f"outs[{l}]", (Lq, topk), torch.int32, dev) for l, o in enumerate(outs)]
+    wsp = _workspace(L.pivot_workspace_size(Lq, H, D, g, topk, C, m, dt), dev, workspace,
+                     L.pivot_workspace_min_size(Lq, H, D, g, topk, C, m, dt))
+    arrs = [_ptr_array(x) for x in (qs, q_scales, ws, ks, k_scales, outs)]
+    fp8 = dt == FP8
+    _check(L.pivot_indexer_layers(nl, f.ctypes.data, arrs[0].ctypes.data,
+                                  arrs[1].ctypes.data if fp8 else None, arrs[2].ctypes.data,
+                                  arrs[3].ctypes.data, arrs[4].ctypes.data if fp8 else None, Lq, H, D,
+                                  g, topk, C, m, dt, arrs[5].ctypes.data, _ptr(wsp), wsp.numel(),
+                                  _stream(stream)))
+    return outs
+
+
+def indexer_decode_layers(qs, ws, ks, cache_len, *, full, topk: int, C: int = 0, mode="refine",
+                          q_scales=None, k_scales=None, outs=None, workspace=None, stream=None):
+    """Cross-layer index reuse stacked on the decode step
+    (pivot_indexer_decode_layers): per layer qs[l] [B,g,H,D], ws[l] [B,g,H],
+    ks[l] [B,Lmax,D] (fp8: scales); cache_len [B] shared.  Returns the list
+    of int32 [B, g, topk] rows per layer."""
+    L = load()
+    nl = len(qs)
+    f = _full_flags(full, nl)
+    q_scales = q_scales or [None] * nl
+    k_scales = k_scales or [None] * nl
+    shape = None
+    for l in range(nl):
+        if not f[l]:
+            continue
+        sh = _decode_inputs(qs[l], ws[l], ks[l], cache_len, q_scales[l], k_scales[l])
+        if shape is not None and sh != shape:
+            raise PivotError(f"layer {l}: every full layer needs the same code type and shape")
+        shape = sh
+        _on_device(q=qs[l], w=ws[l], k_cache=ks[l], cache_len=cache_len, q_scale=q_scales[l],
+                   k_scale=k_scales[l])
+    dt, B, g, H, D, Lmax = shape
+    m = _mode(mode)
+    dev = qs[0].device
+    outs = outs or [None] * nl
+    outs = [_out(o, f"outs[{l}]", (B, g, topk), torch.int32, dev) for l, o in enumerate(outs)]
+    wsp = _workspace(L.pivot_decode_workspace_size(B, Lmax, H, D, g, topk, C, m, dt), dev, workspace)
+    arrs = [_ptr_array(x) for x in (qs, q_scales, ws, ks, k_scales, outs)]
+    fp8 = dt == FP8
+    _check(L.pivot_indexer_decode_layers(nl, f.ctypes.data, arrs[0].ctypes.data,
+                                         arrs[1].ctypes.data if fp8 else None, arrs[2].ctypes.data,
+                                         arrs[3].ctypes.data, arrs[4].ctypes.data if fp8 else None,
+                                         _ptr(cache_len), B, Lmax, H, D, g, topk, C, m, dt,
+                                         arrs[5].ctypes.data, _ptr(wsp), wsp.numel(), _stream(stream)))
+    return outs
 
 
 def indexer_varlen(q, w, k, cu_seqlens, *, g: int, topk: int, C: int = 0, mode="refine",
@@ -557,7 +655,7 @@ def selftest_mfma_layout(device="cuda") -> torch.Tensor:
 
 
 KERNEL_CLASSES = ("proxy_mean", "scan", "select", "refine_score", "member_select", "broadcast",
-                  "decode_scan", "window", "attention")
+                  "decode_scan", "window", "attention", "layer_copy")
 
 
 def profile_enable(on: bool = True) -> None:

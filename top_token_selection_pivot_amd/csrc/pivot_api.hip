@@ -803,6 +803,99 @@ int pivot_dbg_score_rows(const void* q, const float* q_scale, const float* w, co
   return PIVOT_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Cross-layer index reuse stacked on the indexer: full layers run the indexer
+// on their own inputs, every other layer takes the rows of the nearest full
+// layer before it.
+// ---------------------------------------------------------------------------
+// Prefixes the last message with the failing layer.
+static int layer_fail(int st, int layer) {
+  char prev[sizeof g_err];
+  snprintf(prev, sizeof prev, "%s", g_err);
+  return fail(st, "layer %d: %s", layer, prev);
+}
+
+static int validate_layers(int nlayers, const int32_t* full, const void* const* arrays[], int narrays,
+                           int32_t* const* out) {
+  if (nlayers < 1) return fail(PIVOT_ERR_SHAPE, "nlayers=%d must be >= 1", nlayers);
+  if (!full || !out) return fail(PIVOT_ERR_NULL, "full and out must be non-NULL (host arrays)");
+  for (int a = 0; a < narrays; ++a)
+    if (!arrays[a]) return fail(PIVOT_ERR_NULL, "the per-layer pointer arrays must be non-NULL (host arrays)");
+  if (!full[0]) return fail(PIVOT_ERR_PARAM, "layer 0 must run its indexer (full[0] != 0)");
+  for (int l = 0; l < nlayers; ++l)
+    if (!out[l]) return fail(PIVOT_ERR_NULL, "out[%d] must be non-NULL", l);
+  return PIVOT_OK;
+}
+
+static int copy_layer(int32_t* const* out, int l, int src, size_t n, hipStream_t s) {
+  if (out[l] == out[src]) return PIVOT_OK;  // the caller aliased the rows
+  PIVOT_LAUNCH_K(PIVOT_K_LAYER_COPY, s, launch_copy_i32(out[src], out[l], n, s), "layer index copy");
+  return PIVOT_OK;
+}
+
+int pivot_indexer_layers(int nlayers, const int32_t* full, const void* const* q, const float* const* q_scale,
+                         const float* const* w, const void* const* k, const float* const* k_scale, int L, int H,
+                         int D, int g, int topk, int C, int mode, int dtype, int32_t* const* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const void* const* arrays[] = {(const void* const*)q, (const void* const*)w, (const void* const*)k};
+  int st = validate_layers(nlayers, full, arrays, 3, out);
+  if (st) return st;
+  if (dtype == PIVOT_FP8_E4M3 && (!q_scale || !k_scale))
+    return fail(PIVOT_ERR_NULL, "fp8 layers need q_scale and k_scale arrays");
+  // every full layer is checked before anything is enqueued
+  for (int l = 0; l < nlayers; ++l) {
+    if (!full[l]) continue;
+    st = validate_common(q[l], q_scale ? q_scale[l] : nullptr, w[l], k[l], k_scale ? k_scale[l] : nullptr, H, D, g,
+                         topk, C, mode, dtype);
+    if (st) return layer_fail(st, l);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int src = 0;
+  for (int l = 0; l < nlayers; ++l) {
+    if (full[l]) {
+      src = l;
+      st = run_prefill(q[l], q_scale ? q_scale[l] : nullptr, w[l], k[l], k_scale ? k_scale[l] : nullptr, L, H, D, g,
+                       topk, C, mode, dtype, out[l], nullptr, workspace, workspace_bytes, stream);
+      if (st) return st;
+    } else if ((st = copy_layer(out, l, src, (size_t)L * topk, s))) {
+      return st;
+    }
+  }
+  return PIVOT_OK;
+}
+
+int pivot_indexer_decode_layers(int nlayers, const int32_t* full, const void* const* q, const float* const* q_scale,
+                                const float* const* w, const void* const* k_cache, const float* const* k_scale,
+                                const int32_t* cache_len, int B, int Lmax, int H, int D, int g, int topk, int C,
+                                int mode, int dtype, int32_t* const* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const void* const* arrays[] = {(const void* const*)q, (const void* const*)w, (const void* const*)k_cache};
+  int st = validate_layers(nlayers, full, arrays, 3, out);
+  if (st) return st;
+  if (dtype == PIVOT_FP8_E4M3 && (!q_scale || !k_scale))
+    return fail(PIVOT_ERR_NULL, "fp8 layers need q_scale and k_scale arrays");
+  for (int l = 0; l < nlayers; ++l) {
+    if (!full[l]) continue;
+    st = validate_common(q[l], q_scale ? q_scale[l] : nullptr, w[l], k_cache[l], k_scale ? k_scale[l] : nullptr, H,
+                         D, g, topk, C, mode, dtype);
+    if (st) return layer_fail(st, l);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int src = 0;
+  for (int l = 0; l < nlayers; ++l) {
+    if (full[l]) {
+      src = l;
+      st = run_decode(q[l], q_scale ? q_scale[l] : nullptr, w[l], k_cache[l], k_scale ? k_scale[l] : nullptr,
+                      cache_len, B, Lmax, H, D, g, topk, C, mode, dtype, out[l], nullptr, workspace, workspace_bytes,
+                      stream);
+      if (st) return st;
+    } else if ((st = copy_layer(out, l, src, (size_t)B * g * topk, s))) {
+      return st;
+    }
+  }
+  return PIVOT_OK;
+}
+
 // Sparse main attention: chunks per row.  Many rows: one chunk each (no
 // merge); few rows: chunks of kSAttnChunk slots so that about 1024 waves run.
 constexpr int kSAttnChunk = 128;

@@ -219,6 +219,7 @@ hipError_t launch_broadcast(const BroadcastArgs& a, hipStream_t st);
 hipError_t launch_selftest_mfma(int32_t* out, hipStream_t st);
 hipError_t launch_decode_select(const DecSelectArgs& a, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, size_t n, hipStream_t st);
 hipError_t launch_window_union(const WindowArgs& a, hipStream_t st);
 
 constexpr int kDecChunk = 2048;      // keys per decode-scan work item

@@ -1103,6 +1103,29 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// Index rows of one layer handed to another (cross-layer reuse): a plain
+// copy, 16 bytes per thread and step when both ends allow it.
+__global__ void copy_i32_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, size_t n, int vec) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (vec) {
+    const size_t n4 = n / 4;
+    for (; i < n4; i += stride) reinterpret_cast<i32x4*>(dst)[i] = reinterpret_cast<const i32x4*>(src)[i];
+    for (size_t e = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) dst[e] = src[e];
+  } else {
+    for (; i < n; i += stride) dst[i] = src[i];
+  }
+}
+
+hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int vec = ((uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0) ? 1 : 0;
+  const size_t units = vec ? (n + 3) / 4 : n;
+  const int blocks = (int)std::min<size_t>((units + 255) / 256, 4096);
+  hipLaunchKernelGGL(copy_i32_kernel, dim3(blocks), dim3(256), 0, st, src, dst, n, vec);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
   if (n == 0) return hipSuccess;
   const int blocks = (int)std::min<size_t>((n + 255) / 256, 1024);
