@@ -226,9 +226,14 @@ int pivot_indexer_decode_paged(const void* q, const float* q_scale, const float*
  *               (a zero-length sequence is allowed)
  *   out         [cu_seqlens[nseq]][topk + window] int32
  *   window, window_mode as for pivot_indexer_window (window = 0: none)
- * The workspace must hold pivot_varlen_workspace_size bytes (the size for the
- * longest sequence).  All sequences are validated before anything is enqueued;
- * they then run one after another on `stream`.
+ * All sequences are validated before anything is enqueued.  They then run
+ * concurrently on up to four streams the library owns (created once per
+ * device, default priority), forked from `stream` and joined back to it with
+ * events, each stream with its own slice of the workspace: the call is
+ * ordered on `stream` like any other.  pivot_varlen_workspace_size gives room
+ * for one slice per stream (the longest sequence's preferred size each); a
+ * smaller workspace runs fewer sequences at a time, down to one after
+ * another on `stream` (it must hold at least the longest sequence's minimum).
  * ------------------------------------------------------------------------- */
 size_t pivot_varlen_workspace_size(const int64_t* cu_seqlens, int nseq, int H, int D, int g, int topk,
                                    int C, int mode, int dtype);

@@ -225,7 +225,11 @@ def test_varlen_validation(lib):
     assert f([0, 2048, 4096], wsb=1000) == ERR_WORKSPACE
     cu = np.array([0, 100, 100, 3000], np.int64)
     big = lib.pivot_varlen_workspace_size(cu.ctypes.data, 3, 4, 32, 4, 64, 256, pv.REFINE, 0)
-    assert big == lib.pivot_workspace_size(2900, 4, 32, 4, 64, 256, pv.REFINE, 0)
+    one = lib.pivot_workspace_size(2900, 4, 32, 4, 64, 256, pv.REFINE, 0)
+    assert big == 2 * ((one + 255) // 256 * 256)  # a slice per non-empty sequence (at most four)
+    cu8 = np.arange(9, dtype=np.int64) * 100
+    assert lib.pivot_varlen_workspace_size(cu8.ctypes.data, 8, 4, 32, 4, 64, 256, pv.REFINE, 0) == 4 * (
+        (lib.pivot_workspace_size(100, 4, 32, 4, 64, 256, pv.REFINE, 0) + 255) // 256 * 256)
 
 
 def test_paged_decode_validation(lib):

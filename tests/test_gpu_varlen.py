@@ -89,3 +89,23 @@ def test_varlen_fp8_bit_exact(mode):
         else:
             ref, _ = oracle.prefill_groups(v, L, 8, 32, 96, mode, np.arange((L + 7) // 8))
         assert np.array_equal(got[a:b], ref), (mode, i)
+
+
+def test_varlen_rows_do_not_depend_on_the_workspace(batch):
+    """The preferred workspace runs sequences concurrently on the library's
+    streams; the longest sequence's minimum runs them one after another on the
+    caller's stream; both (and two slices) give identical rows."""
+    print("case: varlen with the preferred, a two-slice and the minimum workspace", flush=True)
+    inp, cu = batch
+    d = to_device(inp)
+    kw = dict(g=4, topk=24, C=60, mode="refine")
+    ref = pv.indexer_varlen(d["q"], d["w"], d["k"], cu, **kw)
+    L = pv.load()
+    lmax = int(np.max(np.diff(cu)))
+    mn = L.pivot_workspace_min_size(lmax, 4, 32, 4, 24, 60, pv.REFINE, 0)
+    pref = L.pivot_workspace_size(lmax, 4, 32, 4, 24, 60, pv.REFINE, 0)
+    for nbytes in (mn, 2 * ((pref + 255) // 256 * 256)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        got = pv.indexer_varlen(d["q"], d["w"], d["k"], cu, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), nbytes

@@ -391,8 +391,10 @@ def indexer_varlen(q, w, k, cu_seqlens, *, g: int, topk: int, C: int = 0, mode="
     wm = _window_mode(window_mode)
     out = _out(out, "out", (T, topk + window), torch.int32, q.device)
     _on_device(q=q, w=w, k=k, q_scale=q_scale, k_scale=k_scale)
+    lmax = int(np.max(np.diff(cu))) if nseq else 0
     ws = _workspace(L.pivot_varlen_workspace_size(cu.ctypes.data, nseq, H, D, g, topk, C, m, dt),
-                    q.device, workspace)
+                    q.device, workspace,
+                    L.pivot_workspace_min_size(lmax, H, D, g, topk, C, m, dt) if lmax else 256)
     _check(L.pivot_indexer_varlen(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale),
                                   cu.ctypes.data, nseq, H, D, g, topk, C, m, dt, window, wm,
                                   _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))

@@ -28,6 +28,7 @@ int fail(int status, const char* fmt, ...) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;  // devices whose per-device state the library tracks
 constexpr int kScanRowsPerLaunch = 1024;          // scan rows per launch within a pass
 constexpr size_t kScoreBudget = size_t(2) << 30;  // preferred score bytes per pass
 constexpr int kScanKeyChunk = 2048;              // keys per scan workgroup
@@ -424,6 +425,12 @@ int pivot_indexer(const void* q, const float* q_scale, const float* w, const voi
                      workspace, workspace_bytes, stream, 0, 0, out_scores);
 }
 
+// Several sequences run concurrently: each on one of a few library-owned
+// streams (default priority, created once per device), each stream with its
+// own slice of the workspace, forked from and joined back to the caller's
+// stream with events.
+constexpr int kVarlenStreams = 4;
+
 size_t pivot_varlen_workspace_size(const int64_t* cu_seqlens, int nseq, int H, int D, int g, int topk,
                                    int C, int mode, int dtype) {
   if (!cu_seqlens || nseq < 1) return 0;
@@ -433,8 +440,35 @@ size_t pivot_varlen_workspace_size(const int64_t* cu_seqlens, int nseq, int H, i
     if (n < 0 || n > INT32_MAX) return 0;
     Lmax = std::max<int>(Lmax, (int)n);
   }
-  return Lmax > 0 ? pivot_workspace_size(Lmax, H, D, g, topk, C, mode, dtype) : 256;
+  if (Lmax == 0) return 256;
+  int nonempty = 0;
+  for (int i = 0; i < nseq; ++i) nonempty += cu_seqlens[i + 1] > cu_seqlens[i] ? 1 : 0;
+  const size_t slice = align_up(pivot_workspace_size(Lmax, H, D, g, topk, C, mode, dtype));
+  return slice * (size_t)std::min(kVarlenStreams, nonempty);
 }
+
+namespace {
+std::mutex g_vs_mu;
+hipStream_t g_vs[kMaxDevices][kVarlenStreams] = {};
+bool g_vs_ready[kMaxDevices] = {};
+
+int varlen_streams(hipStream_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PIVOT_ERR_UNSUPPORTED, "device %d beyond the tracked range", dev);
+  std::lock_guard<std::mutex> lk(g_vs_mu);
+  if (!g_vs_ready[dev]) {
+    for (int k = 0; k < kVarlenStreams; ++k) {
+      e = hipStreamCreateWithFlags(&g_vs[dev][k], hipStreamNonBlocking);
+      if (e != hipSuccess) return hip_status(e, "hipStreamCreateWithFlags");
+    }
+    g_vs_ready[dev] = true;
+  }
+  *out = g_vs[dev];
+  return PIVOT_OK;
+}
+}  // namespace
 
 int pivot_indexer_varlen(const void* q, const float* q_scale, const float* w, const void* k,
                          const float* k_scale, const int64_t* cu_seqlens, int nseq, int H, int D, int g,
@@ -454,7 +488,12 @@ int pivot_indexer_varlen(const void* q, const float* q_scale, const float* w, co
   if (st) return st;
   st = validate_window(window, window_mode, topk);
   if (st) return st;
+  if (!workspace) return fail(PIVOT_ERR_NULL, "workspace must be non-NULL");
+  if (!aligned(workspace, kAlign)) return fail(PIVOT_ERR_ALIGN, "workspace must be 256-byte aligned");
   const size_t esz = esize(dtype);
+  const bool dense = mode == PIVOT_MODE_DENSE;
+  std::vector<int> order;
+  size_t need_min = 0;  // the largest minimum workspace of any sequence
   for (int i = 0; i < nseq; ++i) {
     const int64_t t0 = cu_seqlens[i];
     const int L = (int)(cu_seqlens[i + 1] - t0);
@@ -464,25 +503,61 @@ int pivot_indexer_varlen(const void* q, const float* q_scale, const float* w, co
       return fail(PIVOT_ERR_ALIGN, "sequence %d: q and k rows must stay 16-byte aligned", i);
     if ((long long)L * D * esz >= (1ll << 31))
       return fail(PIVOT_ERR_SHAPE, "sequence %d: the key array must stay below 2 GiB", i);
-    const bool dense = mode == PIVOT_MODE_DENSE;
     const PrefillPlan p = plan_prefill(L, H, D, dense ? 1 : g, topk, C, mode, dtype);
-    if (chunk_rows_for(p, workspace_bytes, dense) <= 0)
-      return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu for sequence %d",
-                  workspace_bytes, prefill_bytes(p, std::min(p.G, 8), dense), i);
+    need_min = std::max(need_min, prefill_bytes(p, std::min(p.G, 8), dense));
+    order.push_back(i);
   }
-  // the sequences run one after another on the stream, each through the
-  // whole prefill path with its own causal prefix and groups
-  for (int i = 0; i < nseq; ++i) {
+  if (order.empty()) return PIVOT_OK;
+  // slices: as many concurrent sequences as the workspace holds (at least one)
+  int nslots = std::min<int>(kVarlenStreams, (int)order.size());
+  while (nslots > 1 && (workspace_bytes / nslots) / kAlign * kAlign < need_min) --nslots;
+  const size_t slice = nslots > 1 ? (workspace_bytes / nslots) / kAlign * kAlign : workspace_bytes;
+  if (slice < need_min)
+    return fail(PIVOT_ERR_WORKSPACE, "workspace of %zu bytes is below the minimum %zu", workspace_bytes, need_min);
+  auto run_one = [&](int i, void* ws, size_t wsb, void* strm) {
     const int64_t t0 = cu_seqlens[i];
     const int L = (int)(cu_seqlens[i + 1] - t0);
-    if (L == 0) continue;
-    st = run_prefill((const uint8_t*)q + (size_t)t0 * H * D * esz, q_scale ? q_scale + t0 : nullptr,
-                     w + (size_t)t0 * H, (const uint8_t*)k + (size_t)t0 * D * esz, k_scale ? k_scale + t0 : nullptr,
-                     L, H, D, g, topk, C, mode, dtype, out + (size_t)t0 * (topk + window), nullptr, workspace,
-                     workspace_bytes, stream, window, window_mode);
-    if (st) return st;
+    return run_prefill((const uint8_t*)q + (size_t)t0 * H * D * esz, q_scale ? q_scale + t0 : nullptr,
+                       w + (size_t)t0 * H, (const uint8_t*)k + (size_t)t0 * D * esz, k_scale ? k_scale + t0 : nullptr,
+                       L, H, D, g, topk, C, mode, dtype, out + (size_t)t0 * (topk + window), nullptr, ws, wsb, strm,
+                       window, window_mode);
+  };
+  if (nslots == 1) {  // one after another on the caller's stream
+    for (int i : order)
+      if ((st = run_one(i, workspace, workspace_bytes, stream))) return st;
+    return PIVOT_OK;
   }
-  return PIVOT_OK;
+  hipStream_t* pool = nullptr;
+  if ((st = varlen_streams(&pool))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // longest first, each to the least loaded stream (work ~ L^2)
+  std::sort(order.begin(), order.end(), [&](int x, int y) {
+    return cu_seqlens[x + 1] - cu_seqlens[x] > cu_seqlens[y + 1] - cu_seqlens[y];
+  });
+  hipEvent_t fork = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_status(e, "hipEventCreateWithFlags");
+  e = hipEventRecord(fork, s);
+  for (int j = 0; j < nslots && e == hipSuccess; ++j) e = hipStreamWaitEvent(pool[j], fork, 0);
+  (void)hipEventDestroy(fork);
+  if (e != hipSuccess) return hip_status(e, "varlen fork");
+  std::vector<double> load(nslots, 0.0);
+  for (int i : order) {
+    const int j = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    const double L = (double)(cu_seqlens[i + 1] - cu_seqlens[i]);
+    load[j] += L * L;
+    if ((st = run_one(i, (uint8_t*)workspace + (size_t)j * slice, slice, pool[j]))) break;
+  }
+  // join, also after a failure, so the caller's stream never runs ahead
+  for (int j = 0; j < nslots; ++j) {
+    hipEvent_t done = nullptr;
+    e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(done, pool[j]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, done, 0);
+    if (done) (void)hipEventDestroy(done);
+    if (e != hipSuccess && st == PIVOT_OK) st = hip_status(e, "varlen join");
+  }
+  return st;
 }
 
 int pivot_candidates(const void* q, const float* q_scale, const float* w, const void* k,
@@ -716,7 +791,6 @@ constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace {
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 

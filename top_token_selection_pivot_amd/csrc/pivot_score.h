@@ -30,7 +30,7 @@
 namespace pivot {
 
 constexpr int kScanRows = 8;      // query rows (waves) per scoring workgroup
-constexpr int kRefineSlotMax = 4096;  // candidate slots per Refine workgroup
+constexpr int kRefineSlotMax = kRefineSlotLimit;  // candidate slots per Refine workgroup
 constexpr int kLdsPad = 16;       // bytes of padding per staged key row
 
 // Per-wave query state: A fragments of every head block and contraction step,

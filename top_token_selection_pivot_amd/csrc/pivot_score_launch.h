@@ -2,6 +2,7 @@
 // type; included once per code type so the two compile in parallel.
 #pragma once
 
+#include "pivot_dec_refine.h"
 #include "pivot_score.h"
 
 namespace pivot {
@@ -119,8 +120,17 @@ hipError_t launch_refine_dt(const RefineArgs& a_in, int D, hipStream_t st) {
   const int rows = a.g <= 2 ? 2 : a.g <= 4 ? 4 : kScanRows;
   const int zblocks = (a.g + rows - 1) / rows;
   // all candidates in one workgroup when there are enough groups to fill the
-  // chip (each member's query is then loaded once); 256-slot pieces otherwise
-  a.slot_chunk = (long long)ngrp * zblocks >= 2048 ? min(a.m, kRefineSlotMax) : 256;
+  // chip (each member's query is then loaded once); otherwise the candidates
+  // are split into as few pieces (of at least 256 slots) as bring the launch
+  // to about 2048 workgroups
+  const long long units = (long long)ngrp * zblocks;
+  const int full = min(a.m, kRefineSlotMax);
+  if (units >= 2048) {
+    a.slot_chunk = full;
+  } else {
+    const long long parts = (2048 + units - 1) / units;
+    a.slot_chunk = (int)std::max<long long>(256, ((full + parts - 1) / parts + 255) / 256 * 256);
+  }
   dim3 grid((a.m + a.slot_chunk - 1) / a.slot_chunk, ngrp, zblocks);
   auto f = [&]<int D_, int HB_>() { refine_one<DT, D_, HB_>(a, grid, rows, st); };
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
@@ -131,6 +141,19 @@ template <int DT>
 hipError_t launch_decode_scan_dt(const DecScanArgs& a, int D, hipStream_t st) {
   const int zblocks = a.qr == 1 ? 1 : (a.qr + 1) / 2;
   auto f = [&]<int D_, int HB_>() { decode_one<DT, D_, HB_>(a, zblocks, st); };
+  if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dec_refine_select_dt(const DecRefineArgs& a, int D, hipStream_t st) {
+  const int rows = a.B * a.g;
+  if (rows <= 0) return hipSuccess;
+  auto f = [&]<int D_, int HB_>() {
+    if constexpr (dec_ref_fits<DT, D_>())
+      hipLaunchKernelGGL((dec_refine_select_kernel<DT, D_, HB_>), dim3(rows), dim3(kDecRefThreads), 0, st, a);
+  };
+  if (!dec_ref_fits_rt(DT, D)) return hipErrorInvalidValue;
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
   return hipGetLastError();
 }

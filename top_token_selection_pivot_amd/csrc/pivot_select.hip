@@ -4,6 +4,7 @@
 
 #include "pivot_device.h"
 #include "pivot_kernels.h"
+#include "pivot_select.h"
 
 namespace pivot {
 
@@ -13,6 +14,16 @@ hipError_t launch_refine_bf16(const RefineArgs&, int, hipStream_t);
 hipError_t launch_refine_fp8(const RefineArgs&, int, hipStream_t);
 hipError_t launch_decode_scan_bf16(const DecScanArgs&, int, hipStream_t);
 hipError_t launch_decode_scan_fp8(const DecScanArgs&, int, hipStream_t);
+
+hipError_t launch_dec_refine_select_bf16(const DecRefineArgs&, int, hipStream_t);
+hipError_t launch_dec_refine_select_fp8(const DecRefineArgs&, int, hipStream_t);
+
+bool dec_refine_select_supported(int dtype, int D, int H, int m) {
+  return m <= kRefineSlotLimit && H <= 64 && D * (dtype == kBF16 ? 2 : 1) <= 256;
+}
+hipError_t launch_dec_refine_select(const DecRefineArgs& a, int dtype, int D, hipStream_t st) {
+  return dtype == kBF16 ? launch_dec_refine_select_bf16(a, D, st) : launch_dec_refine_select_fp8(a, D, st);
+}
 
 hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st) {
   return dtype == kBF16 ? launch_scan_bf16(a, D, st) : launch_scan_fp8(a, D, st);
@@ -184,285 +195,6 @@ hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st) {
   else
     hipLaunchKernelGGL(proxy_mean_kernel<kFP8>, dim3(G), dim3(kProxyThreads), 0, st, a);
   return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Exact top-m of one score row (tutorial "Sparse Attention의 Indexer",
-// Figure 1: keep the positions of the m largest scores).
-//
-// Radix select over order-preserving 32-bit keys, most significant digit
-// first, with LDS histograms.  It finds the m-th largest key T and how many
-// keys equal to T are taken; an index-ordered compaction then emits every key
-// above T and the first keys equal to T, so equal scores go to the lower
-// position and the output is ascending.
-//
-// Pass 1 reads the row once (16-byte loads, four in flight per thread) and
-// histograms its top 12 bits.  Every key at or above the threshold bin is then
-// gathered into LDS in index order (a row that fits is staged whole during
-// pass 1); the remaining 20 bits and the emission run on that LDS copy, so a
-// row is read from memory at most twice.  A long row is read about once: a
-// sixteenth of it is sampled first, and pass 1 gathers the keys at or above a
-// conservative bin estimated from the sample while it histograms (pass 2 is
-// needed only when the estimate turns out too high or too low).  If the
-// threshold bin is too crowded for LDS (e.g. a huge run of equal scores), the
-// selection falls back to further passes over the row in memory.
-// ---------------------------------------------------------------------------
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkCap = kSelectCap;  // keys staged in LDS
-constexpr int kTopkBits1 = 12;        // first digit: bits 31..20
-static_assert((1 << kTopkBits1) == kSelectBins1, "first-digit histogram width");
-constexpr int kTopkU = 4;          // 16-byte loads in flight per thread
-constexpr int kTopkSampleMin = 4 * kTopkCap;  // rows this long are sampled first
-
-__device__ inline int ref_count(const int32_t* list, int m, int t) {
-  // number of leading entries of the ascending, -1 padded list that are in [0, t]
-  int lo = 0, hi = m;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const int v = list[mid];
-    if (v >= 0 && v <= t)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  return lo;
-}
-
-__device__ inline int row_length(const TopkArgs& a, int R, const int32_t** list) {
-  *list = nullptr;
-  switch (a.kind) {
-    case kLenPos:
-      return min(R * a.pos_mul + a.pos_add, a.pos_cap) + 1;
-    case kLenCache: {
-      const int nb = a.cache_len[R];
-      return (nb < a.g || nb > a.Lmax) ? 0 : max(0, nb - a.excl);
-    }
-    case kLenDecodeDense: {
-      const int b = R / a.g, i = R % a.g, nb = a.cache_len[b];
-      return (nb < a.g || nb > a.Lmax) ? 0 : max(0, nb - a.g + i + 1 - a.excl);
-    }
-    default: {  // kLenRefine
-      int j, t;
-      if (a.decode) {
-        j = R / a.g;
-        const int nb = a.cache_len[j];
-        if (nb < a.g || nb > a.Lmax) return 0;
-        t = nb - a.g + R % a.g - a.excl;
-      } else {
-        j = R / a.g;
-        t = R - a.excl;
-      }
-      *list = a.map + (size_t)(j - a.map_grp_begin) * a.ldmap;
-      return ref_count(*list, a.ldmap, t);
-    }
-  }
-}
-
-// Refine row R: its group's candidate list and the member's position t;
-// returns 0 (and no list) for a decode sequence with an invalid length.
-__device__ inline int refine_row_list(const TopkArgs& a, int R, const int32_t** list, int* t) {
-  const int j = R / a.g;
-  *list = nullptr;
-  if (a.decode) {
-    const int nb = a.cache_len[j];
-    if (nb < a.g || nb > a.Lmax) return 0;
-    *t = nb - a.g + R % a.g - a.excl;
-  } else {
-    *t = R - a.excl;
-  }
-  *list = a.map + (size_t)(j - a.map_grp_begin) * a.ldmap;
-  return 0;
-}
-
-// The bin (of nbins, a multiple of 256, counted from the top) that holds the
-// rem-th largest key; *above receives the number of keys in higher bins.
-// One wave walks the histogram in rounds of 256 bins from the top (lane l
-// reads the four bins 4l..4l+3 below the round's top with one 16-byte read),
-// so the other waves only wait at the closing barrier.
-template <int NT>
-__device__ inline void find_bin(const uint32_t* hist, int nbins, uint32_t rem, uint32_t* scratch,
-                                uint32_t* sh_bin, uint32_t* sh_above) {
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
-    uint32_t above = 0;
-    for (int k = 0; k < nbins / 256; ++k) {
-      const int top = nbins - 1 - (256 * k + 4 * lane);  // the lane's highest bin
-      const uint4 v = *reinterpret_cast<const uint4*>(&hist[top - 3]);
-      const uint32_t s = v.x + v.y + v.z + v.w;
-      const uint32_t inc = wave_inclusive_sum(s);
-      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
-      if (above + tot >= rem) {
-        uint32_t run = above + inc - s;
-        const uint32_t c[4] = {v.w, v.z, v.y, v.x};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (run < rem && rem <= run + c[e]) {
-            *sh_bin = (uint32_t)(top - e);
-            *sh_above = run;
-          }
-          run += c[e];
-        }
-        break;
-      }
-      above += tot;
-    }
-  }
-  __syncthreads();
-}
-
-// Loads the 4 scores at s0..s0+3 of a row of n (s0 a multiple of 4).
-__device__ inline float4 load4(const float* row, int s0, int n) {
-  if (s0 + 3 < n) return *reinterpret_cast<const float4*>(row + s0);
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (s0 + 0 < n) v.x = row[s0 + 0];
-  if (s0 + 1 < n) v.y = row[s0 + 1];
-  if (s0 + 2 < n) v.z = row[s0 + 2];
-  return v;
-}
-
-__device__ inline float f4(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
-
-// Emits, in index order, the entries of a sequence that are selected by
-// (T, need_eq): keys above T, and the first need_eq keys equal to T.  The
-// sequence is given by get(i) -> (key, slot) for i < cnt; each thread takes
-// 4*kTopkU consecutive entries per round.  A round's selected entries fill a
-// contiguous run of the output: they are placed in LDS (`stage`, kEmitStage
-// words; any overflow is written directly) and then stored coalesced.
-constexpr int kEmitStage = kSelectBins1;
-// The score of every emitted entry also goes to the buffer `srs` (a range of
-// zero bytes when no scores are wanted, so the stores are dropped): written
-// directly, not staged -- a checking aid, not the fast path.
-template <int E, typename Get>
-__device__ inline void emit_selected(int cnt, uint32_t T, uint32_t need_eq, uint32_t m, const int32_t* list,
-                                     int32_t* out, __amdgpu_buffer_rsrc_t srs, uint32_t* scratch, int32_t* stage,
-                                     Get get) {
-  const int tid = threadIdx.x;
-  const uint32_t need_gt = m - need_eq;
-  uint32_t g_gt = 0, g_eq = 0;
-  for (int base = 0; base < cnt; base += E * kTopkThreads) {
-    const int i0 = base + tid * E;
-    uint32_t key[E];
-    int slot[E];
-    get(i0, key, slot);  // entries past cnt get slot -1
-    uint32_t cgt = 0, ceq = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool valid = slot[e] >= 0;
-      cgt += (valid && key[e] > T) ? 1u : 0u;
-      ceq += (valid && key[e] == T) ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t excl = block_exclusive_sum<kTopkThreads>(cgt | (ceq << 16), scratch, &tot);
-    const uint32_t p0 = g_gt + min(g_eq, need_eq);  // the round's first output position
-    uint32_t gt_before = g_gt + (excl & 0xFFFFu), eq_before = g_eq + (excl >> 16);
-    auto put = [&](uint32_t p, int sl, uint32_t k) {
-      if (p >= m) return;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_score(k)), srs, (int)(p * 4), 0, 0);
-      if (p - p0 < (uint32_t)kEmitStage) stage[p - p0] = sl;
-      else out[p] = list ? list[sl] : sl;
-    };
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (slot[e] < 0) continue;
-      if (key[e] > T) {
-        put(gt_before + min(eq_before, need_eq), slot[e], key[e]);
-        ++gt_before;
-      } else if (key[e] == T) {
-        if (eq_before < need_eq) put(gt_before + eq_before, slot[e], key[e]);
-        ++eq_before;
-      }
-    }
-    g_gt += tot & 0xFFFFu;
-    g_eq += tot >> 16;
-    const uint32_t p1 = min(g_gt + min(g_eq, need_eq), m);
-    __syncthreads();
-    for (uint32_t o = tid; o < min(p1 - p0, (uint32_t)kEmitStage); o += kTopkThreads) {
-      const int sl = stage[o];
-      out[p0 + o] = list ? list[sl] : sl;
-    }
-    __syncthreads();
-    if (g_gt >= need_gt && g_eq >= need_eq) break;
-  }
-}
-
-// LDS of the long-row selection.
-struct alignas(16) SelectShared {
-  uint32_t hist[1 << kTopkBits1];
-  uint32_t ckey[kTopkCap];
-  int32_t cslot[kTopkCap];
-  uint32_t scratch[kTopkThreads / kWave + 1];
-  uint32_t sh_bin, sh_above;
-};
-
-// Second half of a long-row selection: the first digit b1 is fixed and rem
-// keys are still needed from bin b1.  Finds the remaining 20 bits in two 10-bit
-// digits (over the ncand keys staged in LDS in index order, or, for
-// ncand < 0, over the row in memory) and emits the selection in index order.
-__device__ __forceinline__ void select_finish(SelectShared& sm, int ncand, uint32_t b1, uint32_t rem, const float* row,
-                              int n, uint32_t m, const int32_t* list, int32_t* out, float* outs) {
-  constexpr int NT = kTopkThreads;
-  const int tid = threadIdx.x;
-  uint32_t prefix = b1 << (32 - kTopkBits1);
-  uint32_t pmask = ~0u << (32 - kTopkBits1);
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    for (int b = tid; b < 1024; b += NT) sm.hist[b] = 0u;
-    __syncthreads();
-    if (ncand >= 0) {
-      for (int c = tid; c < ncand; c += NT) {
-        const uint32_t key = sm.ckey[c];
-        if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 1023u], 1u);
-      }
-    } else {
-      for (int base = 0; base < n; base += kTopkU * NT * 4) {
-        float4 v[kTopkU];
-#pragma unroll
-        for (int u = 0; u < kTopkU; ++u) v[u] = load4(row, base + (u * NT + tid) * 4, n);
-#pragma unroll
-        for (int u = 0; u < kTopkU; ++u) {
-          const int s0 = base + (u * NT + tid) * 4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (s0 + e >= n) continue;
-            const uint32_t key = score_key(f4(v[u], e));
-            if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 1023u], 1u);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    find_bin<NT>(sm.hist, 1024, rem, sm.scratch, &sm.sh_bin, &sm.sh_above);
-    prefix |= sm.sh_bin << shift;
-    pmask |= 1023u << shift;
-    rem -= sm.sh_above;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const uint32_t need_eq = rem;  // keys equal to T to take, lowest positions first
-  int32_t* stage = reinterpret_cast<int32_t*>(sm.hist);
-  const __amdgpu_buffer_rsrc_t srs =
-      __builtin_amdgcn_make_buffer_rsrc(outs ? (void*)outs : (void*)out, 0, outs ? (int)(m * 4) : 0, 0x00020000);
-  if (ncand >= 0) {
-    // four consecutive staged entries per thread: one 16-byte read each
-    emit_selected<4>(ncand, T, need_eq, m, list, out, srs, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(&sm.ckey[i0 < kTopkCap ? i0 : 0]);
-      const int4 sv = *reinterpret_cast<const int4*>(&sm.cslot[i0 < kTopkCap ? i0 : 0]);
-      key[0] = kv.x, key[1] = kv.y, key[2] = kv.z, key[3] = kv.w;
-      slot[0] = sv.x, slot[1] = sv.y, slot[2] = sv.z, slot[3] = sv.w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (i0 + e >= ncand) slot[e] = -1;
-    });
-  } else {
-    emit_selected<4 * kTopkU>(n, T, need_eq, m, list, out, srs, sm.scratch, stage, [&](int i0, uint32_t* key, int* slot) {
-#pragma unroll
-      for (int e = 0; e < 4 * kTopkU; ++e) {
-        const bool valid = i0 + e < n;
-        key[e] = valid ? score_key(row[i0 + e]) : 0u;
-        slot[e] = valid ? i0 + e : -1;
-      }
-    });
-  }
 }
 
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
