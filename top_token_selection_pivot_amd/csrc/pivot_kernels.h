@@ -69,32 +69,6 @@ struct RefineArgs {
   int pool_rows = 0;
 };
 
-// Decode Refine fused with each member's top-k: one workgroup per member row
-// r = b*g + i of a decode step.  The member re-scores its sequence's
-// candidates cand[b] (m slots, ascending, -1 tail) that are <= its own limit
-// and writes its top-k row (and optionally the selected scores).  Cache
-// addressing as in RefineArgs (contiguous [B][Lmax] or a paged pool).
-struct DecRefineArgs {
-  const uint8_t* q;
-  const float* q_scale;
-  const float* w;
-  const uint8_t* k;
-  const float* k_scale;
-  int H, g, Lmax, B;
-  const int32_t* cache_len;
-  const int32_t* cand;
-  int ldc, m;
-  int topk;
-  int32_t* out;
-  long long ldo;
-  float* out_s = nullptr;
-  long long ldos = 0;
-  int excl = 0;
-  const int32_t* bt = nullptr;
-  int bt_stride = 0, page_shift = 0;
-  int pool_rows = 0;
-};
-
 // Decode scan: for each sequence b, qr query rows (rows b*qr .. b*qr+qr-1 of
 // q) scan the sequence's cache_len[b] keys.  qr == 1: the proxy, which sees
 // every key; otherwise the g members, member i seeing keys 0..n_b-g+i.
@@ -240,10 +214,6 @@ hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_refine(const RefineArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_decode_scan(const DecScanArgs& a, int dtype, int D, hipStream_t st);
-// false when the shape is not one the fused kernel is built for (the caller
-// then runs the Refine score kernel and the member top-k separately)
-bool dec_refine_select_supported(int dtype, int D, int H, int m);
-hipError_t launch_dec_refine_select(const DecRefineArgs& a, int dtype, int D, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 hipError_t launch_broadcast(const BroadcastArgs& a, hipStream_t st);
 hipError_t launch_selftest_mfma(int32_t* out, hipStream_t st);

@@ -2,7 +2,6 @@
 // type; included once per code type so the two compile in parallel.
 #pragma once
 
-#include "pivot_dec_refine.h"
 #include "pivot_score.h"
 
 namespace pivot {
@@ -141,19 +140,6 @@ template <int DT>
 hipError_t launch_decode_scan_dt(const DecScanArgs& a, int D, hipStream_t st) {
   const int zblocks = a.qr == 1 ? 1 : (a.qr + 1) / 2;
   auto f = [&]<int D_, int HB_>() { decode_one<DT, D_, HB_>(a, zblocks, st); };
-  if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-template <int DT>
-hipError_t launch_dec_refine_select_dt(const DecRefineArgs& a, int D, hipStream_t st) {
-  const int rows = a.B * a.g;
-  if (rows <= 0) return hipSuccess;
-  auto f = [&]<int D_, int HB_>() {
-    if constexpr (dec_ref_fits<DT, D_>())
-      hipLaunchKernelGGL((dec_refine_select_kernel<DT, D_, HB_>), dim3(rows), dim3(kDecRefThreads), 0, st, a);
-  };
-  if (!dec_ref_fits_rt(DT, D)) return hipErrorInvalidValue;
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -15,16 +15,6 @@ hipError_t launch_refine_fp8(const RefineArgs&, int, hipStream_t);
 hipError_t launch_decode_scan_bf16(const DecScanArgs&, int, hipStream_t);
 hipError_t launch_decode_scan_fp8(const DecScanArgs&, int, hipStream_t);
 
-hipError_t launch_dec_refine_select_bf16(const DecRefineArgs&, int, hipStream_t);
-hipError_t launch_dec_refine_select_fp8(const DecRefineArgs&, int, hipStream_t);
-
-bool dec_refine_select_supported(int dtype, int D, int H, int m) {
-  return m <= kRefineSlotLimit && H <= 64 && D * (dtype == kBF16 ? 2 : 1) <= 256;
-}
-hipError_t launch_dec_refine_select(const DecRefineArgs& a, int dtype, int D, hipStream_t st) {
-  return dtype == kBF16 ? launch_dec_refine_select_bf16(a, D, st) : launch_dec_refine_select_fp8(a, D, st);
-}
-
 hipError_t launch_scan(const ScanArgs& a, int dtype, int D, hipStream_t st) {
   return dtype == kBF16 ? launch_scan_bf16(a, D, st) : launch_scan_fp8(a, D, st);
 }

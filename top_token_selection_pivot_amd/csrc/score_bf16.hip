@@ -11,7 +11,4 @@ hipError_t launch_refine_bf16(const RefineArgs& a, int D, hipStream_t st) {
 hipError_t launch_decode_scan_bf16(const DecScanArgs& a, int D, hipStream_t st) {
   return launch_decode_scan_dt<kBF16>(a, D, st);
 }
-hipError_t launch_dec_refine_select_bf16(const DecRefineArgs& a, int D, hipStream_t st) {
-  return launch_dec_refine_select_dt<kBF16>(a, D, st);
-}
 }  // namespace pivot
