@@ -36,6 +36,7 @@ struct ScanArgs {
   int kc;  // keys per workgroup (multiple of 32)
   float* S;
   long long ldS;
+  int nchunks = 0, nblocks = 0;  // key chunks and row blocks (set by the launcher)
 };
 
 // Members of groups [grp_begin, grp_end) score their group's candidates.

@@ -214,11 +214,21 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
   __amdgpu_buffer_rsrc_t krs; // keys: the chunk (scan) or the whole key array (Refine)
   __amdgpu_buffer_rsrc_t crs; // Refine: candidate positions of slots [k0, k1)
   __amdgpu_buffer_rsrc_t ksr; // fp8 key scales (empty for bf16)
+  int gj = 0;                 // Refine: this workgroup's group
   if constexpr (!GATHER) {
-    const int rb = a.row_begin + blockIdx.y * ROWS;
+    // XCD-aware order: workgroups are dealt to the chip's eight XCDs in turn
+    // (linear id i goes to XCD i % 8), so the i-th workgroup takes the
+    // (i % 8) * n/8 + i/8 -th (chunk, row block) in chunk-major order: the
+    // workgroups on one XCD work through consecutive row blocks of the same
+    // key chunk together and read its keys through that XCD's L2
+    const int per = gridDim.x / 8;
+    const int lin = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    if (lin >= a.nchunks * a.nblocks) return;
+    const int bx = lin / a.nblocks, by = lin % a.nblocks;
+    const int rb = a.row_begin + by * ROWS;
     const int rlast = min(rb + ROWS, a.row_end) - 1;
     const int lim = min(rlast * a.pos_mul + a.pos_add, a.pos_cap) + 1;  // keys 0..lim-1
-    k0 = blockIdx.x * a.kc;
+    k0 = bx * a.kc;
     if (k0 >= lim) return;
     k1 = min(k0 + a.kc, lim);
     r = rb + wid;
@@ -230,7 +240,9 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
     crs = krs;
     ksr = make_rsrc(DT == kFP8 ? a.k_scale + k0 : a.S, DT == kFP8 ? (uint32_t)(k1 - k0) * 4u : 0u);
   } else {
-    const int j = a.grp_begin + blockIdx.y;
+    const int bx = blockIdx.x, bz = blockIdx.z;
+    gj = a.grp_begin + blockIdx.y;
+    const int j = gj;
     int row0, nmem, ncand, nkeys;
     size_t keybase = 0;
     if (a.kind == 0) {
@@ -247,10 +259,10 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
       nkeys = a.bt ? a.pool_rows : nb;  // paged: the whole pool, slots translated below
       keybase = a.bt ? 0 : (size_t)j * a.Lmax;
     }
-    k0 = blockIdx.x * a.slot_chunk;
+    k0 = bx * a.slot_chunk;
     if (k0 >= ncand) return;
     k1 = min(k0 + a.slot_chunk, ncand);
-    const int mem = blockIdx.z * ROWS + wid;
+    const int mem = bz * ROWS + wid;
     active = mem < nmem;
     r = row0 + (active ? mem : 0);
     nvalid = active ? k1 : 0;
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
       int v = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, e * 4, 0, 0);
       if constexpr (std::is_same_v<Args, RefineArgs>) {
         if (a.bt) {
-          const int j = a.grp_begin + blockIdx.y;
+          const int j = gj;
           v = max(v, 0);
           const int pg = a.bt[(size_t)j * a.bt_stride + (v >> a.page_shift)];
           v = (unsigned)pg < (unsigned)(a.pool_rows >> a.page_shift)

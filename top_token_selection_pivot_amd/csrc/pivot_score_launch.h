@@ -106,7 +106,10 @@ hipError_t launch_scan_dt(const ScanArgs& a_in, int D, hipStream_t st) {
   const int rlast = a.row_end - 1;
   const int lim = min(rlast * a.pos_mul + a.pos_add, a.pos_cap) + 1;
   if (nrows <= 0 || lim <= 0) return hipSuccess;  // no row sees any key
-  dim3 grid((lim + a.kc - 1) / a.kc, (nrows + kScanRows - 1) / kScanRows);
+  a.nchunks = (lim + a.kc - 1) / a.kc;
+  a.nblocks = (nrows + kScanRows - 1) / kScanRows;
+  const long long n = (long long)a.nchunks * a.nblocks;
+  dim3 grid((unsigned)((n + 7) / 8 * 8));  // a multiple of the eight XCDs
   auto f = [&]<int D_, int HB_>() { scan_one<DT, D_, HB_>(a, grid, st); };
   if (!dispatch_shape<DT>(D, a.H, f)) return hipErrorInvalidValue;
   return hipGetLastError();
