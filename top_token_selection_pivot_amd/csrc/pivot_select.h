@@ -30,7 +30,8 @@ namespace pivot {
 // threshold bin is too crowded for LDS (e.g. a huge run of equal scores), the
 // selection falls back to further passes over the row in memory.
 // ---------------------------------------------------------------------------
-constexpr int kTopkThreads = 1024;
+constexpr int kTopkThreads = 1024;     // threads of a one-row workgroup (few rows)
+constexpr int kTopkThreadsMany = 512;  // with many rows: two workgroups share a compute unit
 constexpr int kTopkCap = kSelectCap;  // keys staged in LDS
 constexpr int kTopkBits1 = 12;        // first digit: bits 31..20
 static_assert((1 << kTopkBits1) == kSelectBins1, "first-digit histogram width");
@@ -213,7 +214,7 @@ struct alignas(16) SelectShared {
   uint32_t hist[1 << kTopkBits1];
   uint32_t ckey[kTopkCap];
   int32_t cslot[kTopkCap];
-  uint32_t scratch[kTopkThreads / kWave + 1];
+  uint32_t scratch[kTopkThreads / kWave + 1];  // one word per wave of the largest workgroup
   uint32_t sh_bin, sh_above;
 };
 

@@ -187,8 +187,8 @@ hipError_t launch_proxy_mean(const ProxyArgs& a, int dtype, hipStream_t st) {
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
-  constexpr int NT = kTopkThreads;
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
   constexpr int NB1 = 1 << kTopkBits1;
   __shared__ SelectShared sm;
 
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   } else {
     ncand = -1;  // fall back to passes over the row in memory
   }
-  select_finish(sm, ncand, b1, rem, row, n, m, list, out, outs);
+  select_finish<NT>(sm, ncand, b1, rem, row, n, m, list, out, outs);
 }
 
 // ---------------------------------------------------------------------------
@@ -629,13 +629,17 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArg
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.nrows <= 0) return hipSuccess;
   // rows whose length is bounded by the candidate list (Refine) fit one wave;
-  // with few rows a whole workgroup per row finishes sooner
+  // with few rows a whole workgroup per row finishes sooner; with at least
+  // two rows per compute unit, half-size workgroups let two rows share a
+  // compute unit, so one row's barrier waits overlap the other's work
   const bool small = a.kind == kLenRefine && a.ldmap <= kSmallMax && a.nrows >= 1024;
   if (small)
     hipLaunchKernelGGL(topk_small_kernel, dim3((a.nrows + kSmallWaves - 1) / kSmallWaves),
                        dim3(kSmallWaves * kWave), 0, st, a);
+  else if (a.nrows >= 512)
+    hipLaunchKernelGGL(topk_kernel<kTopkThreadsMany>, dim3(a.nrows), dim3(kTopkThreadsMany), 0, st, a);
   else
-    hipLaunchKernelGGL(topk_kernel, dim3(a.nrows), dim3(kTopkThreads), 0, st, a);
+    hipLaunchKernelGGL(topk_kernel<kTopkThreads>, dim3(a.nrows), dim3(kTopkThreads), 0, st, a);
   return hipGetLastError();
 }
 
