@@ -292,7 +292,8 @@ int pivot_indexer_decode_layers(int nlayers, const int32_t* full, const void* co
  *        e.g. pivot_indexer's rows); entries outside [0, seq_len) are skipped
  *        and a row with none gets zeros
  *   scale  > 0, applied to every dot product (usually 1/sqrt(d))
- * Scores and sums are binary32; the softmax weights enter the value product
+ * One sequence's key rows (and its value rows) must stay below 2 GiB
+ * (PIVOT_ERR_SHAPE).  Scores and sums are binary32; the softmax weights enter the value product
  * as two bf16 terms, so the result is close to binary32 accuracy.  Few rows
  * split their slots over several waves and need a workspace of
  * pivot_sparse_attention_workspace_size bytes (0: none needed).

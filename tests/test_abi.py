@@ -200,6 +200,8 @@ def test_sparse_attention_validation(lib):
     assert f(stride=100) == ERR_PARAM          # sequences would overlap
     assert f(scale=0.0) == ERR_PARAM
     assert f(out=FAKE + 4) == ERR_ALIGN
+    assert f(seq_len=1 << 23, stride=1 << 23) == ERR_SHAPE  # 2^23 rows of 256 bytes: 2 GiB
+    assert f(seq_len=(1 << 23) - 1, stride=1 << 23) == ERR_WORKSPACE  # just below 2 GiB passes
     assert f() == ERR_WORKSPACE                 # 64 rows: chunks merged through the workspace
     assert lib.pivot_sparse_attention_workspace_size(64, 64, 128, 2048) > 0
     assert lib.pivot_sparse_attention_workspace_size(4096, 64, 128, 2048) == 0  # one chunk per row

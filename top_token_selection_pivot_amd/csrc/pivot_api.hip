@@ -1008,8 +1008,10 @@ int pivot_sparse_attention(const void* q, const void* k, const void* v, const in
                 seq_len, seq_stride);
   if ((R - 1) / rows_per_seq > 0 && seq_stride < seq_len)
     return fail(PIVOT_ERR_PARAM, "seq_stride=%lld is below seq_len=%d with several sequences", seq_stride, seq_len);
-  if ((long long)seq_len * std::max(d, dv) * 2 >= (1ll << 32))
-    return fail(PIVOT_ERR_SHAPE, "one sequence's key or value rows must stay below 4 GiB");
+  // below 2 GiB: row offsets fit a signed 32-bit product, and the offset the
+  // gathers use for skipped entries lies past every buffer's range
+  if ((long long)seq_len * std::max(d, dv) * 2 >= (1ll << 31))
+    return fail(PIVOT_ERR_SHAPE, "one sequence's key or value rows must stay below 2 GiB");
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PIVOT_ERR_PARAM, "scale must be finite and > 0");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(idx, 4))
     return fail(PIVOT_ERR_ALIGN, "q, k, v and out must be 16-byte aligned, idx 4-byte aligned");
