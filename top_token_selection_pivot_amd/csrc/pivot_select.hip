@@ -98,6 +98,11 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
     for (int h = tid; h < a.H; h += kProxyThreads) a.wbar[(size_t)j * a.H + h] = a.w[(size_t)r0 * a.H + h];
     return;
   }
+  // With a power-of-two member count the division is a product with 1/n:
+  // both round the same exact quotient once, so the result is identical.
+  const bool pow2 = (n & (n - 1)) == 0;
+  const float inv_n = __uint_as_float((uint32_t)(127 - __builtin_ctz((unsigned)n)) << 23);  // 2^-log2(n)
+  auto mean_of = [&](float sum) { return pow2 ? sum * inv_n : __fdiv_rn(sum, (float)n); };
   // Members are read kProxyU at a time so that their loads are in flight
   // together (past the last member the load repeats it and is not used; for
   // the weights +0 is added instead, which leaves a running sum unchanged: a
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
 #pragma unroll
       for (int u = 0; u < kProxyU; ++u) s = __fadd_rn(s, t0 + u < n ? x[u] : 0.f);
     }
-    a.wbar[(size_t)j * a.H + h] = __fdiv_rn(s, (float)n);
+    a.wbar[(size_t)j * a.H + h] = mean_of(s);
   }
   // means of this thread's chunks, members added in ascending position
   float mean[kProxyMaxCPT][kProxyChunk];
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
     }
 #pragma unroll
     for (int e = 0; e < kProxyChunk; ++e) {
-      mean[i][e] = __fdiv_rn(acc[e], (float)n);
+      mean[i][e] = mean_of(acc[e]);
       amax = fmaxf(amax, fabsf(mean[i][e]));
     }
   }
