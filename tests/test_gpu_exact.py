@@ -321,6 +321,24 @@ def test_long_rows_selection(kmax):
     assert np.array_equal(dense[rows], oracle.dense_rows(v, rows, topk))
 
 
+@pytest.mark.parametrize("kmax", [4, 0])
+def test_long_rows_few_rows_selection(kmax):
+    # fewer than 512 proxy rows in a launch take the 1024-thread long-row
+    # top-k (many rows take the 512-thread one above): g = 128 at L = 40000
+    # gives 313 proxy rows, the last 74 of them 30720 scores or longer
+    print(f"case: L=40000 H=8 D=64 integer inputs, g=128, kmax={kmax}, few long rows", flush=True)
+    L, g, topk, C = 40000, 128, 2048, 4096
+    inp = synth.small_integer(L, 8, 64, seed=43, qmax=4, kmax=kmax, wmax=3)
+    v = oracle.View.of(inp)
+    G = (L + g - 1) // g
+    cand = pv.candidates(*(to_device(inp)[x] for x in ("q", "w", "k")), g=g, topk=topk, C=C,
+                         mode="refine").cpu().numpy()
+    rng = np.random.default_rng(10)
+    for j in sorted({0, 238, 239, G - 2, G - 1} | set(rng.integers(240, G, 4).tolist())):
+        _, rc, _ = oracle.group(v, j * g, j * g, min(g, L - j * g), topk, C, "refine")
+        assert np.array_equal(cand[j], rc), j
+
+
 def test_deterministic_repeat():
     # float inputs (where a different summation order would show), ten calls
     # each: a prefill whose long rows take the sampled top-k, and a decode step
