@@ -49,11 +49,15 @@ __device__ inline uint32_t bf16x2_rne(float x0, float x1) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){x0, x1}, bf16x2_t));
 }
 
+// The softmax runs in base-2 units: a score is scaled once by scale * log2(e),
+// so every weight is one exp2 of a difference (exp(scale*x - c) = 2^(x' - c')).
 // The running maximum of a head moves only when a tile's maximum exceeds it by
-// more than kLazyMax (natural-log units), so the output is rarely rescaled;
-// the weights exp(x - m) then stay below e^kLazyMax.  The result is the same
-// in exact arithmetic: the output and the sum always refer to the same m.
-constexpr float kLazyMax = 8.f;
+// more than kLazyMax (base-2 units), so the output is rarely rescaled; the
+// weights 2^(x - m) then stay below 2^kLazyMax.  The result is the same in
+// exact arithmetic: the output and the sum always refer to the same m.
+constexpr float kLazyMax = 12.f;
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A workgroup holds NW = Hq / 32 waves on the same (chunk, row); wave w takes
 // heads 32 w .. 32 w + 31.  With 64 heads a wave keeps its registers under
@@ -102,7 +106,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW))
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running maximum (base-2 units) and sum
+  const float sl2 = a.scale * kLog2e;
 
   // lane n (and n + 32) holds the position of slot n of the tile at t0
   auto load_pos = [&](int t0) { return t0 + n < s1 ? idx[t0 + n] : -1; };
@@ -142,21 +147,29 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW))
     }
     // online softmax of head n: accumulator i holds key row 8 (i / 4) + 4 hf + i % 4
     float mt = -INFINITY;
+    if (vmask == 0xFFFFFFFFu) {  // the usual tile: every key valid
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
-      sc[i] = ((vmask >> key) & 1u) ? sc[i] * a.scale : -INFINITY;
-      mt = fmaxf(mt, sc[i]);
+      for (int i = 0; i < 16; ++i) {
+        sc[i] *= sl2;
+        mt = fmaxf(mt, sc[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+        sc[i] = ((vmask >> key) & 1u) ? sc[i] * sl2 : -INFINITY;
+        mt = fmaxf(mt, sc[i]);
+      }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const bool grow = mt > m + kLazyMax;  // with m = -inf: any valid key
     const float mn = grow ? mt : m;
-    const float alpha = grow ? __expf(m - mn) : 1.f;  // 0 on the first tile with a valid key
+    const float alpha = grow ? exp2_fast(m - mn) : 1.f;  // 0 on the first tile with a valid key
     const float base = mn == -INFINITY ? 0.f : mn;
     float ls = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sc[i] = __expf(sc[i] - base);
+      sc[i] = exp2_fast(sc[i] - base);
       ls += sc[i];
     }
     ls += __shfl_xor(ls, 32);
@@ -252,8 +265,9 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW))
   }
 }
 
-// Merges the chunks of one (row, head): with M the largest chunk maximum,
-// out = sum_c exp(m_c - M) o_c / sum_c exp(m_c - M) l_c (zeros when the row
+// Merges the chunks of one (row, head): with M the largest chunk maximum
+// (base-2 units, as the chunks store them),
+// out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c (zeros when the row
 // selected nothing).  A thread takes four value columns of one (row, head) and
 // up to kMergeChunks chunks at a time: every chunk's maximum, sum and partial
 // output are loaded before any is used (indices clamped, so no load is
@@ -288,7 +302,7 @@ __global__ __launch_bounds__(kMergeThreads) void sattn_combine_kernel(SAttnArgs 
       Mn = fmaxf(Mn, mc[i]);
     }
     if (Mn == -INFINITY) continue;  // nothing selected so far
-    const float sc = __expf(M - Mn);  // 0 on the first round that sees a slot
+    const float sc = exp2_fast(M - Mn);  // 0 on the first round that sees a slot
     L *= sc;
     acc.x *= sc;
     acc.y *= sc;
@@ -296,7 +310,7 @@ __global__ __launch_bounds__(kMergeThreads) void sattn_combine_kernel(SAttnArgs 
     acc.w *= sc;
 #pragma unroll
     for (int i = 0; i < kMergeChunks; ++i) {
-      const float wgt = __expf(mc[i] - Mn);
+      const float wgt = exp2_fast(mc[i] - Mn);
       L += wgt * lc[i];
       acc.x += wgt * oc[i].x;
       acc.y += wgt * oc[i].y;
