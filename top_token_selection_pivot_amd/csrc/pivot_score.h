@@ -467,8 +467,8 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
   __shared__ __attribute__((aligned(16))) uint8_t ring2[R > 2 ? W : 1][R > 2 ? G::STAGE_BYTES : 16];
   __shared__ uint32_t hist[QR][NB];
   __shared__ __attribute__((aligned(16))) float sbuf[W][QR][G::BLOCK_PAIRS * G::PAIR_KEYS];
-  __shared__ uint32_t scratch[NT / kWave + 1];
   __shared__ int sh_b, sh_off;
+  __shared__ uint32_t sh_lo, sh_hi;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, n = lane & 31;
@@ -478,34 +478,39 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
     const int nb = a.cache_len[b];
     return (nb < a.g || nb > a.Lmax) ? 0u : (uint32_t)(nb + G::PAIR_KEYS - 1) / G::PAIR_KEYS;
   };
-  // this workgroup's run [lo, hi) of the batch's pairs, and where it starts
-  uint32_t total = 0;
-  for (int b0 = 0; b0 < a.B; b0 += NT) {
-    uint32_t tot;
-    block_exclusive_sum<NT>(b0 + tid < a.B ? seq_pairs(b0 + tid) : 0u, scratch, &tot);
-    total += tot;
-  }
-  const uint32_t lo = (uint32_t)((uint64_t)total * blockIdx.x / gridDim.x);
-  const uint32_t hi = (uint32_t)((uint64_t)total * (blockIdx.x + 1) / gridDim.x);
-  if (lo == hi) return;
-  {
+  // this workgroup's run [lo, hi) of the batch's pairs and where it starts,
+  // found by the first wave alone (prefix sums over the sequences, a wave's
+  // width at a time) while the others clear the histograms
+  if (wid == 0) {
+    uint32_t total = 0;
+    for (int b0 = 0; b0 < a.B; b0 += kWave) {
+      const uint32_t inc = wave_inclusive_sum(b0 + lane < a.B ? seq_pairs(b0 + lane) : 0u);
+      total += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+    }
+    const uint32_t lo_ = (uint32_t)((uint64_t)total * blockIdx.x / gridDim.x);
+    const uint32_t hi_ = (uint32_t)((uint64_t)total * (blockIdx.x + 1) / gridDim.x);
     uint32_t base = 0;
-    for (int b0 = 0; b0 < a.B; b0 += NT) {
-      const int b = b0 + tid;
-      const uint32_t p = b < a.B ? seq_pairs(b) : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_exclusive_sum<NT>(p, scratch, &tot);
-      if (p && base + ex <= lo && lo < base + ex + p) {
-        sh_b = b;
-        sh_off = (int)(lo - base - ex);
+    for (int b0 = 0; b0 < a.B && base <= lo_; b0 += kWave) {
+      const int bb = b0 + lane;
+      const uint32_t p = bb < a.B ? seq_pairs(bb) : 0u;
+      const uint32_t inc = wave_inclusive_sum(p);
+      const uint32_t ex = inc - p;
+      if (p && base + ex <= lo_ && lo_ < base + ex + p) {
+        sh_b = bb;
+        sh_off = (int)(lo_ - base - ex);
       }
-      base += tot;
-      if (base > lo) break;
+      base += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+    }
+    if (lane == 0) {
+      sh_lo = lo_;
+      sh_hi = hi_;
     }
   }
   for (int i = 0; i < QR; ++i)
     for (int e = tid; e < NB; e += NT) hist[i][e] = 0u;
   __syncthreads();
+  const uint32_t lo = sh_lo, hi = sh_hi;
+  if (lo == hi) return;
   int b = __builtin_amdgcn_readfirstlane(sh_b), off = __builtin_amdgcn_readfirstlane(sh_off);
   uint32_t left = hi - lo;
 
