@@ -224,6 +224,10 @@ hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, size_t n, hipStream
 hipError_t launch_window_union(const WindowArgs& a, hipStream_t st);
 
 constexpr int kDecChunk = 2048;      // keys per decode-scan work item
+#ifndef PIVOT_DEC_SEGMENT_PAIRS
+#define PIVOT_DEC_SEGMENT_PAIRS 32
+#endif
+constexpr int kDecSegmentPairs = PIVOT_DEC_SEGMENT_PAIRS;  // a decode segment's set-up, in pairs of work
 constexpr int kRefineSlotLimit = 4096;  // candidate slots one Refine workgroup holds
 constexpr int kSelectCap = kSelectCapDefault;
 constexpr int kSelectBins1 = 4096;   // bins of the first radix digit (top 12 bits)

@@ -478,13 +478,23 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
     const int nb = a.cache_len[b];
     return (nb < a.g || nb > a.Lmax) ? 0u : (uint32_t)(nb + G::PAIR_KEYS - 1) / G::PAIR_KEYS;
   };
-  // this workgroup's run [lo, hi) of the batch's pairs and where it starts,
-  // found by the first wave alone (prefix sums over the sequences, a wave's
-  // width at a time) while the others clear the histograms
+  // Runs are cut in work units: every non-empty sequence counts its pairs plus
+  // kDecSegmentPairs units for the set-up of a segment (query rows, the ring's
+  // first stages, the histogram flush), which stand for no keys.  A run that
+  // reaches into a further sequence thus takes correspondingly fewer pairs,
+  // and the workgroups finish together.
+  constexpr uint32_t SEG = kDecSegmentPairs;
+  auto seq_units = [&](int b) -> uint32_t {
+    const uint32_t p = seq_pairs(b);
+    return p ? p + SEG : 0u;
+  };
+  // this workgroup's run [lo, hi) of the batch's work units and where it
+  // starts, found by the first wave alone (prefix sums over the sequences, a
+  // wave's width at a time) while the others clear the histograms
   if (wid == 0) {
     uint32_t total = 0;
     for (int b0 = 0; b0 < a.B; b0 += kWave) {
-      const uint32_t inc = wave_inclusive_sum(b0 + lane < a.B ? seq_pairs(b0 + lane) : 0u);
+      const uint32_t inc = wave_inclusive_sum(b0 + lane < a.B ? seq_units(b0 + lane) : 0u);
       total += (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
     }
     const uint32_t lo_ = (uint32_t)((uint64_t)total * blockIdx.x / gridDim.x);
@@ -492,7 +502,7 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
     uint32_t base = 0;
     for (int b0 = 0; b0 < a.B && base <= lo_; b0 += kWave) {
       const int bb = b0 + lane;
-      const uint32_t p = bb < a.B ? seq_pairs(bb) : 0u;
+      const uint32_t p = bb < a.B ? seq_units(bb) : 0u;
       const uint32_t inc = wave_inclusive_sum(p);
       const uint32_t ex = inc - p;
       if (p && base + ex <= lo_ && lo_ < base + ex + p) {
@@ -511,12 +521,22 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
   __syncthreads();
   const uint32_t lo = sh_lo, hi = sh_hi;
   if (lo == hi) return;
-  int b = __builtin_amdgcn_readfirstlane(sh_b), off = __builtin_amdgcn_readfirstlane(sh_off);
+  int b = __builtin_amdgcn_readfirstlane(sh_b);
+  uint32_t vo = (uint32_t)__builtin_amdgcn_readfirstlane(sh_off);  // units into sequence b
   uint32_t left = hi - lo;
 
   while (left > 0 && b < a.B) {
     const int nb = a.cache_len[b];
-    const int np = (int)min((uint32_t)((nb + G::PAIR_KEYS - 1) / G::PAIR_KEYS - off), left);
+    const uint32_t take = min(seq_units(b) - vo, left);  // this sequence's units in the run
+    const int off = (int)(vo > SEG ? vo - SEG : 0u);     // its first pair
+    const int np = (int)(vo + take > SEG ? vo + take - SEG : 0u) - off;
+    left -= take;
+    vo = 0;
+    if (np <= 0) {  // the run holds only set-up units of this sequence
+      while (left > 0 && ++b < a.B && seq_pairs(b) == 0) {
+      }
+      continue;
+    }
     const int k0 = off * G::PAIR_KEYS;
     const int k1 = min(k0 + np * G::PAIR_KEYS, nb);
 
@@ -662,8 +682,6 @@ __global__ __launch_bounds__((DecGeom<DT, D, QR>::THREADS)) void decode_scan_ker
       }
       __syncthreads();
     }
-    left -= (uint32_t)np;
-    off = 0;
     while (left > 0 && ++b < a.B && seq_pairs(b) == 0) {
     }
   }
