@@ -73,9 +73,11 @@ struct RefineArgs {
 // Decode scan: for each sequence b, qr query rows (rows b*qr .. b*qr+qr-1 of
 // q) scan the sequence's cache_len[b] keys.  qr == 1: the proxy, which sees
 // every key; otherwise the g members, member i seeing keys 0..n_b-g+i.
-// Each workgroup takes (sequence, chunk of kDecChunk keys) work items; `hist`
-// (optional, zeroed beforehand) receives for every output row the histogram of
-// the top 12 bits of its scores' order-preserving keys, [B*qr][4096].
+// Persistent workgroups take equal runs of work over the batch's pairs of
+// 32-key tiles (a sequence's pairs plus kDecSegmentPairs units for a segment's
+// set-up); `hist` (optional, zeroed beforehand) receives for every output row
+// the histogram of the top 12 bits of its scores' order-preserving keys,
+// [B*qr][4096].
 struct DecScanArgs {
   const uint8_t* q;
   const float* q_scale;
@@ -223,7 +225,6 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t launch_copy_i32(const int32_t* src, int32_t* dst, size_t n, hipStream_t st);
 hipError_t launch_window_union(const WindowArgs& a, hipStream_t st);
 
-constexpr int kDecChunk = 2048;      // keys per decode-scan work item
 #ifndef PIVOT_DEC_SEGMENT_PAIRS
 #define PIVOT_DEC_SEGMENT_PAIRS 32
 #endif
