@@ -15,6 +15,7 @@ import oracle
 import synth
 import top_token_selection_pivot_amd as pv
 from conftest import GOLDEN
+import parity
 from parity import to_device
 
 pytestmark = pytest.mark.gpu
@@ -294,6 +295,50 @@ def test_long_exact_sampled_groups():
     for j in groups:
         ref, _, _ = oracle.group(v, j * g, j * g, g, topk, C, "refine")
         assert np.array_equal(out[j * g:(j + 1) * g], ref), j
+
+
+@pytest.fixture(scope="module")
+def tiny16k():
+    return synth.tiny_integer(L=16384, H=4, D=32, seed=77)
+
+
+@pytest.mark.parametrize("g,W,wmode", [(8, 0, "shared"), (16, 0, "shared"), (8, 300, "excluded"),
+                                       (8, 100, "shared")])
+def test_refine_2048_groups_bit_exact(tiny16k, g, W, wmode):
+    """Refine at 2048 (group, member block) units, the launch shape in which
+    every Refine workgroup takes all of its group's candidates, with the
+    member top-k on rows of C=256 candidates (one wave per row).  Integer
+    inputs: every row, and every returned score, equals the oracle's.  The
+    excluded window of 300 leaves the first groups without candidates, so
+    their members' rows hold only -1 (and the window)."""
+    print(f"case: L=16384 H=4 D=32 Refine g={g} k=64 C=256, window {W} {wmode}", flush=True)
+    L, topk, C = 16384, 64, 256
+    inp = tiny16k
+    d = to_device(inp)
+    kw = dict(window=W, window_mode=wmode) if W else dict(return_scores=True)
+    res = pv.indexer(d["q"], d["w"], d["k"], g=g, topk=topk, C=C, mode="refine", **kw)
+    torch.cuda.synchronize()
+    v = oracle.View.of(inp)
+    G = L // g
+    chunks = np.array_split(np.arange(G), parity.THREADS)
+    excl = W if wmode == "excluded" else 0
+    parts = parity.pmap(lambda c: oracle.prefill_groups(v, L, g, topk, C, "refine", c, excl=excl)[0], chunks)
+    ref = np.concatenate(parts)
+    if W:
+        ref = oracle.window_union(ref, np.arange(L), W)
+        got = res.cpu().numpy()
+    else:
+        got, sc = res[0].cpu().numpy(), res[1].cpu().numpy()
+    bad = np.nonzero((got != ref).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5]}"
+    if W:
+        return
+    def row_scores(rows):
+        for t in rows:
+            sel = got[t][got[t] >= 0]
+            assert np.array_equal(sc[t][:len(sel)].astype(np.float64), oracle.score_list(v, int(t), sel)), t
+            assert np.all(np.isnan(sc[t][len(sel):])), t
+    parity.pmap(row_scores, np.array_split(np.arange(L), parity.THREADS))
 
 
 @pytest.mark.parametrize("kmax", [4, 0])

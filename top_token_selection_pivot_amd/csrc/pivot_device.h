@@ -142,6 +142,14 @@ __device__ constexpr int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
+// A raw buffer resource over `bytes` bytes at `base`: loads past the range
+// return zeros and stores past it are dropped by the hardware range check.
+constexpr uint32_t kBufferFlags = 0x00020000;  // raw 32-bit buffer, range-checked
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+
 // ---------------------------------------------------------------------------
 // Order-preserving 32-bit key of a float score (larger score -> larger key);
 // -0 is folded onto +0 so equal scores get equal keys.

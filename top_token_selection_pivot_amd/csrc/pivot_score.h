@@ -154,11 +154,6 @@ struct KeyTile {
 // ---------------------------------------------------------------------------
 constexpr int kScanStageTiles = 8;    // full-prefix scan: fewer barriers per key
 constexpr int kRefineStageTiles = 4;  // Refine: chunks of candidate slots are short
-constexpr uint32_t kBufferFlags = 0x00020000;  // raw 32-bit buffer, range-checked
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
-}
 
 // Interleaving hint for one tile step: the DS reads of the next tile, the 16
 // contractions and the previous tile's epilogue alternate.

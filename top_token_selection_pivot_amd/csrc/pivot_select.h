@@ -1,7 +1,7 @@
-// pivot_select.h -- the exact top-m selection building blocks shared by the
-// selection kernels (pivot_select.hip) and the fused decode Refine kernel
-// (pivot_score.h): radix digits over order-preserving keys in LDS, the
-// threshold-bin search and the index-ordered emission.
+// pivot_select.h -- the exact top-m selection building blocks of the
+// selection kernels (pivot_select.hip): radix digits over order-preserving
+// keys in LDS, the threshold-bin search, the index-ordered emission and the
+// one-wave selection of short rows.
 #pragma once
 
 #include "pivot_device.h"
@@ -289,5 +289,226 @@ __device__ __forceinline__ void select_finish(SelectShared& sm, int ncand, uint3
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Top-m of short rows (n <= 4096, e.g. a member's candidates): one wave per
+// row.  The row's keys live in registers (64 per lane) and the radix select
+// runs 8-bit digits against a private 256-bin LDS histogram per wave, starting
+// below the bits all of the row's keys share.  After the first digit the keys
+// of the threshold bin (usually a few percent of the row) are compacted into
+// LDS and the remaining digits run on that short list.  The index-ordered
+// emission is a wave-level scan, so no workgroup barrier is needed.  Lane l
+// holds elements 256*i + 4*l .. 256*i + 4*l + 3 of chunk i.
+// ---------------------------------------------------------------------------
+constexpr int kSmallMax = 4096;
+constexpr int kSmallWaves = 4;
+constexpr int kSmallChunks = kSmallMax / 256;
+constexpr int kSmallCand = 512;  // threshold-bin keys a wave compacts for its later digits
+
+__device__ inline uint32_t wave_exclusive_sum(uint32_t v, uint32_t* total) {
+  const uint32_t inc = wave_inclusive_sum(v);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)inc, kWave - 1);
+  return inc - v;
+}
+
+// Maximum over the wave (DPP row shifts and row broadcasts, then lane 63).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));   // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));   // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));   // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));   // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+// Orders this wave's LDS accesses across lanes (wave-scope fence + barrier).
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The top-m of one short row by one wave: the scores of slots [0, lmax)
+// (lmax <= kSmallMax) in `row`, the positions of the slots in `list`
+// (ascending, -1 padded); slots whose position is not in [0, t] are excluded.
+// Writes m positions (and their scores if outs is non-null) to out, -1 / NaN
+// padded.  cand (kSmallCand words) is this wave's LDS.
+__device__ inline void wave_row_select(const float* row, const int32_t* list, int lmax, int t, uint32_t m,
+                                       int32_t* out, float* outs, uint32_t* cand) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[kSmallChunks * 4];
+  int32_t val[kSmallChunks * 4];
+  // every load of the row and of its positions is issued before any is used
+  // (range-checked buffer loads: no branch, so no wait between them)
+  const __amdgpu_buffer_rsrc_t rrow = make_rsrc(row, (uint32_t)lmax * 4u);
+  const __amdgpu_buffer_rsrc_t rlist = make_rsrc(list, (uint32_t)lmax * 4u);
+  float4 v[kSmallChunks];
+  i32x4 p[kSmallChunks];
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int s0 = c * 256 + lane * 4;
+    v[c] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rrow, s0 * 4, 0, 0));
+    p[c] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rlist, s0 * 4, 0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their first use
+  uint32_t cnt_le = 0;
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    const int s0 = c * 256 + lane * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[c * 4 + e] = score_key(f4(v[c], e));
+      val[c * 4 + e] = p[c][e];
+      cnt_le += (s0 + e < lmax && p[c][e] >= 0 && p[c][e] <= t) ? 1u : 0u;
+    }
+  }
+  uint32_t n_u;
+  wave_exclusive_sum(cnt_le, &n_u);
+  const int n = (int)n_u;
+  if (n <= (int)m) {
+    for (int s = lane; s < (int)m; s += kWave) {
+      out[s] = s < n ? list[s] : -1;
+      if (outs) outs[s] = s < n ? row[s] : no_score();
+    }
+    return;
+  }
+  // Entries past the row get key 0.  No score has key 0 (it would be a NaN),
+  // so they rank below every entry of the row: they never reach the threshold
+  // and are never emitted.
+  uint32_t kmax = 0u, kmin1 = 0xFFFFFFFFu;  // kmin1: smallest key - 1 of the row
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = c * 256 + lane * 4 + e < n ? key[c * 4 + e] : 0u;
+      key[c * 4 + e] = k;
+      kmax = max(kmax, k);
+      kmin1 = min(kmin1, k - 1u);
+    }
+  kmax = wave_max_u32(kmax);
+  const uint32_t kmin = ~wave_max_u32(~kmin1) + 1u;
+  // bits above the highest bit where the row's keys differ are common to all
+  const int top = kmin == kmax ? 0 : 32 - __clz((int)(kmin ^ kmax));  // undetermined low bits
+  const uint32_t pmask = top == 32 ? 0u : ~0u << top;
+
+  // T, the m-th largest key, by a binary search over the undetermined bits,
+  // most significant first: T takes bit b when at least m keys are >= T | 2^b.
+  // `above` counts the keys >= T + 2^(b+1) (fewer than m) and `inwin` those in
+  // [T, T + 2^(b+1)), the keys not yet decided.  Counting is a compare and an
+  // add per key and a wave sum per bit (no atomics); it runs over the
+  // registers until the undecided keys fit the wave's LDS list, then over
+  // that list.  At the end `above` counts the keys > T.
+  uint32_t T = kmax & pmask, above = 0, inwin = (uint32_t)n;
+  int b = top - 1;
+  bool narrowed = false;
+  while (b >= 0 && inwin > (uint32_t)kSmallCand) {
+    const uint32_t Tc = T | (1u << b);
+    // four independent partial counts, so that each compare's lane mask is
+    // consumed a few instructions later rather than by the next one
+    uint32_t c4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kSmallChunks * 4; ++j) c4[j & 3] += key[j] >= Tc ? 1u : 0u;
+    uint32_t c = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+    wave_exclusive_sum(c, &c);
+    if (c >= m) {
+      T = Tc;
+      inwin = c - above;
+    } else {
+      inwin = above + inwin - c;
+      above = c;
+    }
+    --b;
+    if (!narrowed && b >= 0) {
+      // The first bit usually sets apart a few outlying keys; the rest then
+      // share several more leading bits, which one min/max pass over the
+      // undecided keys skips at once (the range they span never holds a key
+      // outside them, so `above` and `inwin` stay as they are).
+      narrowed = true;
+      const uint32_t wmask = ~0u << (b + 1);  // b + 1 <= 31 here
+      uint32_t hi = 0u, nlo = 0u;             // largest key, complement of the smallest
+#pragma unroll
+      for (int j = 0; j < kSmallChunks * 4; ++j) {
+        const bool in = key[j] != 0u && (key[j] & wmask) == T;
+        hi = max(hi, in ? key[j] : 0u);
+        nlo = max(nlo, in ? ~key[j] : 0u);
+      }
+      hi = wave_max_u32(hi);
+      const uint32_t lo = ~wave_max_u32(nlo);
+      const int t2 = hi == lo ? 0 : 32 - __clz((int)(hi ^ lo));
+      if (t2 < b + 1) {
+        T = t2 == 0 ? hi : hi & (~0u << t2);
+        b = t2 - 1;
+      }
+    }
+  }
+  if (b >= 0) {
+    // compact the undecided keys (any order: only their values matter); a
+    // valid key is never 0, so the entries past the row stay out
+    const uint32_t wmask = b + 1 >= 32 ? 0u : ~0u << (b + 1);
+    uint32_t base = 0;
+#pragma unroll
+    for (int j = 0; j < kSmallChunks * 4; ++j) {
+      const bool hit = key[j] != 0u && (key[j] & wmask) == T;
+      const unsigned long long mk = __ballot(hit);
+      if (hit) cand[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = key[j];
+      base += (uint32_t)__popcll(mk);
+    }
+    wave_sync();
+    uint32_t ck[kSmallCand / kWave];
+#pragma unroll
+    for (int j = 0; j < kSmallCand / kWave; ++j) ck[j] = (uint32_t)(j * kWave + lane) < base ? cand[j * kWave + lane] : 0u;
+    wave_sync();
+    const uint32_t base_above = above;  // keys above the list's range
+    for (; b >= 0; --b) {
+      const uint32_t Tc = T | (1u << b);
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < kSmallCand / kWave; ++j) c += ck[j] >= Tc ? 1u : 0u;
+      wave_exclusive_sum(c, &c);
+      c += base_above;
+      if (c >= m)
+        T = Tc;
+      else
+        above = c;
+    }
+  }
+  const uint32_t need_eq = m - above;
+
+  // emission in index order (entries past the row hold key 0 < T)
+  uint32_t g_gt = 0, g_eq = 0;
+#pragma unroll
+  for (int c = 0; c < kSmallChunks; ++c) {
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cgt += key[c * 4 + e] > T ? 1u : 0u;
+      ceq += key[c * 4 + e] == T ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t excl = wave_exclusive_sum(cgt | (ceq << 16), &tot);
+    uint32_t gt_before = g_gt + (excl & 0xFFFFu), eq_before = g_eq + (excl >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t kk = key[c * 4 + e];
+      if (kk > T) {
+        const uint32_t p = gt_before + min(eq_before, need_eq);
+        if (p < m) {
+          out[p] = val[c * 4 + e];
+          if (outs) outs[p] = key_score(kk);
+        }
+        ++gt_before;
+      } else if (kk == T) {
+        const uint32_t p = gt_before + eq_before;
+        if (eq_before < need_eq && p < m) {
+          out[p] = val[c * 4 + e];
+          if (outs) outs[p] = key_score(kk);
+        }
+        ++eq_before;
+      }
+    }
+    g_gt += tot & 0xFFFFu;
+    g_eq += tot >> 16;
+  }
+}
 
 }  // namespace pivot
