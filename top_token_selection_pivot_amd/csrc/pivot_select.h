@@ -474,7 +474,11 @@ __device__ inline void wave_row_select(const float* row, const int32_t* list, in
   }
   const uint32_t need_eq = m - above;
 
-  // emission in index order (entries past the row hold key 0 < T)
+  // emission in index order (entries past the row hold key 0 < T).  No
+  // branch per entry: every entry's store is issued, the unselected ones at
+  // an offset past the row's range, which the buffer range check drops.
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(out, m * 4u);
+  const __amdgpu_buffer_rsrc_t routs = make_rsrc(outs, outs ? m * 4u : 0u);
   uint32_t g_gt = 0, g_eq = 0;
 #pragma unroll
   for (int c = 0; c < kSmallChunks; ++c) {
@@ -490,21 +494,16 @@ __device__ inline void wave_row_select(const float* row, const int32_t* list, in
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t kk = key[c * 4 + e];
-      if (kk > T) {
-        const uint32_t p = gt_before + min(eq_before, need_eq);
-        if (p < m) {
-          out[p] = val[c * 4 + e];
-          if (outs) outs[p] = key_score(kk);
-        }
-        ++gt_before;
-      } else if (kk == T) {
-        const uint32_t p = gt_before + eq_before;
-        if (eq_before < need_eq && p < m) {
-          out[p] = val[c * 4 + e];
-          if (outs) outs[p] = key_score(kk);
-        }
-        ++eq_before;
-      }
+      const bool gt = kk > T, eq = kk == T;
+      // a key above T goes after every earlier key above T and the first
+      // need_eq keys equal to T; a key equal to T is taken while fewer than
+      // need_eq equal keys precede it
+      const uint32_t p = gt ? gt_before + min(eq_before, need_eq) : gt_before + eq_before;
+      const uint32_t off = (gt || (eq && eq_before < need_eq)) ? p * 4u : m * 4u;
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)val[c * 4 + e], rout, (int)off, 0, 0);
+      if (outs) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_score(kk)), routs, (int)off, 0, 0);
+      gt_before += gt ? 1u : 0u;
+      eq_before += eq ? 1u : 0u;
     }
     g_gt += tot & 0xFFFFu;
     g_eq += tot >> 16;

@@ -404,8 +404,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 __global__ __launch_bounds__(kSmallWaves * kWave) void topk_small_kernel(TopkArgs a) {
   __shared__ uint32_t cand_all[kSmallWaves][kSmallCand];
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int i = blockIdx.x * kSmallWaves + wid;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, so the row's
+  const int i = blockIdx.x * kSmallWaves + wid;                       // addresses are scalar
   if (i >= a.nrows) return;
   const int R = a.row_begin + i;
   const float* row = a.S + (long long)i * a.ldS;
