@@ -134,14 +134,14 @@ __device__ inline void find_bin(const uint32_t* hist, int nbins, uint32_t rem, u
   __syncthreads();
 }
 
-// Loads the 4 scores at s0..s0+3 of a row of n (s0 a multiple of 4).
+// Loads the 4 scores at s0..s0+3 of a row of n (s0 a multiple of 4), zeros at
+// and past n.  One range-checked 16-byte buffer load: the hardware checks each
+// dword of it against the range (a load straddling the end returns the dwords
+// before it and zeros after), so no branch, and several such loads stay in
+// flight together.  `row` must be wave-uniform (a scalar descriptor).
 __device__ inline float4 load4(const float* row, int s0, int n) {
-  if (s0 + 3 < n) return *reinterpret_cast<const float4*>(row + s0);
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (s0 + 0 < n) v.x = row[s0 + 0];
-  if (s0 + 1 < n) v.y = row[s0 + 1];
-  if (s0 + 2 < n) v.z = row[s0 + 2];
-  return v;
+  return __builtin_bit_cast(
+      float4, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(row, (uint32_t)n * 4u), s0 * 4, 0, 0));
 }
 
 __device__ inline float f4(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
