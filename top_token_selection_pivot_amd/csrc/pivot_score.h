@@ -287,19 +287,32 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
   // a paged cache the candidate positions become pool rows here; a page id
   // outside the pool gives the row just past it, which reads as zeros.
   if constexpr (GATHER) {
-    for (int e = tid; e < k1 - k0; e += NT) {
-      int v = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, e * 4, 0, 0);
+    // the chunk's positions are loaded in batches of 8 per thread, every load
+    // of a batch issued before any is used (one memory latency per 8 NT
+    // positions, not per NT); slots past the chunk read as 0 through the
+    // range check and are not stored
+    constexpr int CB = 8;
+    for (int base = 0; base < k1 - k0; base += CB * NT) {
+      int cv[CB];
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        cv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(crs, (base + tid + i * NT) * 4, 0, 0);
       if constexpr (std::is_same_v<Args, RefineArgs>) {
         if (a.bt) {
           const int j = gj;
-          v = max(v, 0);
-          const int pg = a.bt[(size_t)j * a.bt_stride + (v >> a.page_shift)];
-          v = (unsigned)pg < (unsigned)(a.pool_rows >> a.page_shift)
-                  ? (pg << a.page_shift) + (v & ((1 << a.page_shift) - 1))
-                  : a.pool_rows;
+#pragma unroll
+          for (int i = 0; i < CB; ++i) {
+            const int v = max(cv[i], 0);
+            const int pg = a.bt[(size_t)j * a.bt_stride + (v >> a.page_shift)];
+            cv[i] = (unsigned)pg < (unsigned)(a.pool_rows >> a.page_shift)
+                        ? (pg << a.page_shift) + (v & ((1 << a.page_shift) - 1))
+                        : a.pool_rows;
+          }
         }
       }
-      cand_s[e] = v;
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        if (base + tid + i * NT < k1 - k0) cand_s[base + tid + i * NT] = cv[i];
     }
     __syncthreads();
   }
