@@ -388,6 +388,13 @@ __global__ __launch_bounds__(ROWS * kWave) void score_block_kernel(Args a) {
   for (int sb = k0; sb < k1; sb += STAGE_KEYS) {
     const uint8_t* st = lds + buf * STAGE_BYTES;
     load_b(st, 0, b0);
+#if PIVOT_SCAN_SCHED
+    // Refine and fp8: all of the first tile's fragment reads go out together
+    // right after the barrier (the stage was not readable before it), rather
+    // than each just ahead of the contraction that uses it.  (The bf16
+    // full-prefix scan has no registers to spare for this: it would spill.)
+    if constexpr (GATHER || DT == kFP8) __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
     for (int t = 0; t < ST; t += 2) {
       // even tile: contract it, finish and store the pair before it
