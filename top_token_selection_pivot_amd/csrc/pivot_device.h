@@ -180,37 +180,6 @@ __device__ inline uint16_t f32_to_bf16_rne(float x) {
   return (uint16_t)(u >> 16);
 }
 
-// OCP E4M3FN code -> float (exact).
-__device__ inline float e4m3_to_f32(uint8_t c) {
-  const int e = (c >> 3) & 15, m = c & 7;
-  float mag = (e == 0) ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
-  if (e == 15 && m == 7) mag = __uint_as_float(0x7FC00000u);
-  return (c & 0x80) ? -mag : mag;
-}
-
-// binary32 -> E4M3FN, round to nearest even, saturating to +-448.  The value is
-// scaled by a power of two so that the 3 kept mantissa bits become the integer
-// part, rounded with rintf (ties to even), and re-assembled.
-__device__ inline uint8_t f32_to_e4m3_rne_sat(float x) {
-  if (x != x) return 0x7F;
-  const uint8_t sign = (__float_as_uint(x) >> 31) ? 0x80 : 0x00;
-  const float a = fabsf(x);
-  if (a >= 448.0f) return sign | 0x7E;
-  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9
-    const int m = (int)rintf(ldexpf(a, 9));  // 0..8; 8 is the smallest normal (code 0x08)
-    return sign | (uint8_t)m;
-  }
-  int E = ilogbf(a);  // a = 1.f * 2^E, E in [-6, 8]
-  int m = (int)rintf(ldexpf(a, 3 - E));  // in [8, 16]
-  if (m == 16) {
-    m = 8;
-    ++E;
-  }
-  int code = ((E + 7) << 3) | (m - 8);
-  if (code > 0x7E) code = 0x7E;
-  return sign | (uint8_t)code;
-}
-
 // ---------------------------------------------------------------------------
 // Wave / block scans.
 // ---------------------------------------------------------------------------

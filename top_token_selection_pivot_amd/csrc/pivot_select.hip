@@ -76,8 +76,12 @@ __device__ inline void chunk_values(const ChunkRaw& r, float* x) {
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      x[e] = __fmul_rn(r.s, e4m3_to_f32((uint8_t)((uint32_t)r.lo[e >> 2] >> (8 * (e & 3)))));
+    for (int q = 0; q < 4; ++q) {  // exact decode (hardware E4M3FN conversion)
+      x[4 * q + 0] = __fmul_rn(r.s, __builtin_amdgcn_cvt_f32_fp8(r.lo[q], 0));
+      x[4 * q + 1] = __fmul_rn(r.s, __builtin_amdgcn_cvt_f32_fp8(r.lo[q], 1));
+      x[4 * q + 2] = __fmul_rn(r.s, __builtin_amdgcn_cvt_f32_fp8(r.lo[q], 2));
+      x[4 * q + 3] = __fmul_rn(r.s, __builtin_amdgcn_cvt_f32_fp8(r.lo[q], 3));
+    }
   }
 }
 
@@ -173,9 +177,17 @@ __global__ __launch_bounds__(kProxyThreads) void proxy_mean_kernel(ProxyArgs a) 
     for (int i = 0; i < kProxyMaxCPT; ++i) {
       const int c = tid + i * kProxyThreads;
       if (c >= nch) continue;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      // E4M3FN codes, round to nearest even, saturating at +-448: the
+      // hardware conversion of the value clamped to +-448
+      auto sat = [](float v) { return fminf(fmaxf(v, -448.f), 448.f); };
+      uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) w[e >> 2] |= (uint32_t)f32_to_e4m3_rne_sat(__fdiv_rn(mean[i][e], sp)) << (8 * (e & 3));
+      for (int q = 0; q < 4; ++q) {
+        const float* v = &mean[i][4 * q];
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(sat(__fdiv_rn(v[0], sp)), sat(__fdiv_rn(v[1], sp)), 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(sat(__fdiv_rn(v[2], sp)), sat(__fdiv_rn(v[3], sp)), pk, true);
+        w[q] = (uint32_t)pk;
+      }
       *reinterpret_cast<i32x4*>(a.qbar + (size_t)j * HD + (size_t)c * kProxyChunk) =
           i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
